@@ -1,0 +1,164 @@
+"""Python face of the plain CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg are the only callers. The HIP library and its binding never
+import this package, and this package imports nothing from them.
+
+The functions take and return numpy arrays. bf16 tensors are uint16 bit
+patterns; gate weights and combined rows are float64. Each function states
+the passage it follows in oracle.c, which it calls one-to-one.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Optional
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+# ORACLE_LIB points the wrapper at another build of oracle.c (the mutation
+# test uses it to load deliberately broken copies).
+LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+SRC_PATH = os.path.join(_HERE, "oracle.c")
+
+GCC_FLAGS = ["-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math",
+             "-fno-builtin", "-shared", "-fPIC", "-Wall", "-Wextra"]
+
+
+def build(verbose: bool = False) -> str:
+    """Compile oracle.c into liboracle.so with gcc (single-threaded, no SIMD intrinsics)."""
+    tmp = LIB_PATH + ".tmp"
+    cmd = ["gcc", *GCC_FLAGS, SRC_PATH, "-o", tmp, "-lm"]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            build()
+        lib = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        lib.oracle_route_topk.argtypes = [P, P, i64, i32, i32, i32, P, P]
+        lib.oracle_dispatch_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P]
+        lib.oracle_dispatch_permute.argtypes = [P, P, i64, i32, i32, P, i64]
+        lib.oracle_combine_reduce.argtypes = [P, i64, P, P, P, P, i64, i32, i32, P, i64, P]
+        lib.oracle_bf16_round.argtypes = [ctypes.c_double]
+        lib.oracle_bf16_round.restype = ctypes.c_uint16
+        lib.oracle_bf16_round_array.argtypes = [P, i64, P]
+        for f in ("oracle_route_topk", "oracle_dispatch_layout",
+                  "oracle_dispatch_permute", "oracle_combine_reduce"):
+            getattr(lib, f).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: Optional[np.ndarray]):
+    return None if a is None else a.ctypes.data
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def route_topk(logits: np.ndarray, bias: Optional[np.ndarray], k: int,
+               normalize: bool = True):
+    """Top-k experts per token (ties to the lower id, descending order) and
+    float64 gate weights from the unbiased logits; see oracle_route_topk."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    bias = None if bias is None else _c(bias, np.float32)
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    rc = _load().oracle_route_topk(_ptr(logits), _ptr(bias), T, E, k,
+                                   1 if normalize else 0, _ptr(idx), _ptr(w))
+    if rc != 0:
+        raise ValueError("oracle_route_topk rejected its arguments")
+    return idx, w
+
+
+def dispatch_layout(topk_idx: np.ndarray, E: int, R: int, capacity: int = -1,
+                    with_send_src: bool = True) -> dict:
+    """Counts, offsets, token-order capacity drops and send positions; see
+    oracle_dispatch_layout."""
+    topk_idx = _c(topk_idx, np.int32)
+    T, k = topk_idx.shape
+    out = {
+        "expert_demand": np.empty(E, np.int32),
+        "expert_counts": np.empty(E, np.int32),
+        "expert_offsets": np.empty(E + 1, np.int32),
+        "dest_counts": np.empty(R, np.int32),
+        "dest_offsets": np.empty(R + 1, np.int32),
+        "pos": np.empty((T, k), np.int32),
+        "send_src": np.full(T * k, -1, np.int32) if with_send_src else None,
+    }
+    rc = _load().oracle_dispatch_layout(
+        _ptr(topk_idx), T, E, k, R, capacity,
+        _ptr(out["expert_demand"]), _ptr(out["expert_counts"]),
+        _ptr(out["expert_offsets"]), _ptr(out["dest_counts"]),
+        _ptr(out["dest_offsets"]), _ptr(out["pos"]), _ptr(out["send_src"]))
+    if rc != 0:
+        raise ValueError("oracle_dispatch_layout rejected its arguments")
+    return out
+
+
+def dispatch_permute(x: np.ndarray, pos: np.ndarray, send_rows: int,
+                     fill: int = 0) -> np.ndarray:
+    """send[pos[t, j]] = x[t] for kept replicas; other rows hold `fill`."""
+    x = _c(x, np.uint16)
+    pos = _c(pos, np.int32)
+    T, H = x.shape
+    k = pos.shape[1]
+    send = np.full((send_rows, H), fill, np.uint16)
+    rc = _load().oracle_dispatch_permute(_ptr(x), _ptr(pos), T, H, k, _ptr(send), send_rows)
+    if rc != 0:
+        raise ValueError("oracle_dispatch_permute: position outside the send buffer")
+    return send
+
+
+def combine_reduce(y: np.ndarray, pos: np.ndarray, w: np.ndarray,
+                   shared: Optional[np.ndarray], residual: Optional[np.ndarray],
+                   tokens: Optional[np.ndarray] = None) -> np.ndarray:
+    """float64 gate-weighted sum over kept replicas + shared + residual; see
+    oracle_combine_reduce. With `tokens`, only those rows are computed."""
+    y = _c(y, np.uint16)
+    pos = _c(pos, np.int32)
+    w = _c(w, np.float64)
+    T, k = pos.shape
+    H = y.shape[1]
+    shared = None if shared is None else _c(shared, np.uint16)
+    residual = None if residual is None else _c(residual, np.uint16)
+    tok = None if tokens is None else _c(tokens, np.int64)
+    rows = T if tok is None else tok.shape[0]
+    out = np.empty((rows, H), np.float64)
+    rc = _load().oracle_combine_reduce(
+        _ptr(y), y.shape[0], _ptr(pos), _ptr(w), _ptr(shared), _ptr(residual),
+        T, H, k, _ptr(tok), rows, _ptr(out))
+    if rc != 0:
+        raise ValueError("oracle_combine_reduce rejected its arguments")
+    return out
+
+
+def bf16_round(a) -> np.ndarray:
+    """Nearest bf16 (ties to even) of each float64 value, as uint16 bits."""
+    a = _c(a, np.float64)
+    out = np.empty(a.shape, np.uint16)
+    _load().oracle_bf16_round_array(_ptr(a), a.size, _ptr(out))
+    return out
+
+
+def bf16_to_f64(bits) -> np.ndarray:
+    """Exact value of bf16 bit patterns as float64."""
+    b = _c(bits, np.uint16)
+    return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)

@@ -1,0 +1,344 @@
+/*
+ * oracle.c -- plain, slow CPU oracle for the MoE dispatch/combine path.
+ *
+ * TEST INFRASTRUCTURE ONLY. Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load this library. The product path
+ * (the HIP library and its Python binding) never calls it, and the two share
+ * no code: not a header, helper, table or constant.
+ *
+ * Every function is single-threaded, loops over tokens in order and writes
+ * the definition out directly. Values (gate weights, combined rows) are
+ * computed in double precision; the selection score is the single-precision
+ * sum logit + bias, because that float decides the integer result (which
+ * experts are picked) and both sides must take that decision in the same
+ * precision.
+ *
+ * Sources (pages are cited by title and section):
+ *  - ai-from-scratch "19. All-to-all", intro: every token carries a list of
+ *    expert IDs, is shipped to those experts, and the results are mixed.
+ *  - same page, "Why the router can ruin your day": a per-expert bias enters
+ *    only the top-k decision, never the mix weights; an expert over capacity
+ *    drops tokens, which then count as having skipped that expert.
+ *  - aicassindra "gpu_moe_all_to_all", "Two collectives per layer, and what
+ *    each one moves": k replicas out, k partial results back along the
+ *    inverse permutation, scaled by the gate weights at the origin; counts
+ *    per destination precede the payload.
+ *  - same page, "Bucketing: cut the message count, not the byte count":
+ *    sort by destination and build the offset table so that each
+ *    destination's rows are contiguous.
+ *  - "MoE All-to-All Dispatch and Ragged Routing", "Returning Tokens to the
+ *    Original GPU": the residual x + dx is formed at the origin; "Fixed
+ *    Capacity vs. Ragged Routing": per-sender-expert slots under a capacity
+ *    factor, excess dropped; ragged routing is dropless.
+ *  - ai-from-scratch "19. All-to-all", section on 512 experts (10 routed +
+ *    1 shared): the shared expert is always active.
+ *
+ * Build: gcc -std=c11 -O2 -ffp-contract=off -fno-fast-math -shared -fPIC.
+ * Parity pins for every function live in the CPU test suite; none of the
+ * functions here is unpinned.
+ */
+#include <float.h>
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#if !defined(FLT_EVAL_METHOD) || FLT_EVAL_METHOD != 0
+#error "the oracle needs float arithmetic evaluated in float (FLT_EVAL_METHOD == 0)"
+#endif
+
+/* ------------------------------------------------------------------ */
+/* bf16 <-> real                                                       */
+/* ------------------------------------------------------------------ */
+
+/* A bf16 value is the upper half of an IEEE binary32 pattern. */
+static double bf16_value(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/*
+ * Round a real number to the nearest bf16 value, ties to even, straight from
+ * the format's definition: 8 significant bits, exponent range of binary32,
+ * subnormal spacing 2^-133, overflow to infinity. NaN becomes a quiet NaN
+ * with the input's sign.
+ */
+uint16_t oracle_bf16_round(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000u : 0u;
+    if (isnan(v))
+        return (uint16_t)(sign | 0x7FC0u);
+    if (isinf(v))
+        return (uint16_t)(sign | 0x7F80u);
+    double a = fabs(v);
+    if (a == 0.0)
+        return sign;
+    int e = ilogb(a);             /* 2^e <= a < 2^(e+1) */
+    if (e < -126)
+        e = -126;                 /* subnormal range: fixed spacing */
+    double q = ldexp(1.0, e - 7); /* spacing of bf16 values near a */
+    double r = nearbyint(a / q) * q;   /* default mode: nearest, ties even */
+    const double max_bf16 = ldexp(255.0, 120);   /* (2 - 2^-7) * 2^127 */
+    if (r > max_bf16)
+        return (uint16_t)(sign | 0x7F80u);
+    float f = (float)r;           /* exact: r has at most 8 significant bits */
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    return (uint16_t)(sign | (u >> 16));
+}
+
+void oracle_bf16_round_array(const double *in, int64_t n, uint16_t *out)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = oracle_bf16_round(in[i]);
+}
+
+/* ------------------------------------------------------------------ */
+/* route: top-k selection and gate weights                             */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Is score a (expert ia) ranked strictly above score b (expert ib)?
+ * Real-valued comparison (-0 equals +0); any NaN ranks below every number,
+ * including -inf, and all NaNs tie; ties go to the smaller expert id.
+ */
+static int ranks_above(float a, int ia, float b, int ib)
+{
+    int na = isnan(a), nb = isnan(b);
+    if (!na && nb)
+        return 1;
+    if (na && !nb)
+        return 0;
+    if (!na && !nb) {
+        if (a > b)
+            return 1;
+        if (a < b)
+            return 0;
+    }
+    return ia < ib;
+}
+
+/*
+ * For each token t: score s_e = logit[t][e] + bias[e] in float; select the k
+ * experts with the highest scores, in descending rank order. Gate weights
+ * use the unbiased logits of the selected experts only:
+ *   normalize != 0: w_j = exp(l_j - m) / sum_i exp(l_i - m) over the k
+ *                   selected (softmax renormalised over the selection);
+ *   normalize == 0: w_j = exp(l_j - M) / sum over all E experts of
+ *                   exp(l_e - M) (full softmax, not renormalised).
+ * Returns 0, or -1 on bad sizes or allocation failure.
+ */
+int oracle_route_topk(const float *logits, const float *bias, int64_t T,
+                      int32_t E, int32_t k, int32_t normalize,
+                      int32_t *topk_idx, double *topk_w)
+{
+    if (T < 0 || E <= 0 || k <= 0 || k > E)
+        return -1;
+    float *s = (float *)malloc((size_t)E * sizeof(float));
+    char *taken = (char *)malloc((size_t)E);
+    if (!s || !taken) {
+        free(s);
+        free(taken);
+        return -1;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        const float *row = logits + t * (int64_t)E;
+        for (int32_t e = 0; e < E; ++e) {
+            s[e] = bias ? row[e] + bias[e] : row[e];
+            taken[e] = 0;
+        }
+        int32_t *idx = topk_idx + t * (int64_t)k;
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t best = -1;
+            for (int32_t e = 0; e < E; ++e) {
+                if (taken[e])
+                    continue;
+                if (best < 0 || ranks_above(s[e], e, s[best], best))
+                    best = e;
+            }
+            taken[best] = 1;
+            idx[j] = best;
+        }
+        double *w = topk_w + t * (int64_t)k;
+        if (normalize) {
+            double m = -INFINITY;
+            for (int32_t j = 0; j < k; ++j)
+                if ((double)row[idx[j]] > m)
+                    m = (double)row[idx[j]];
+            double sum = 0.0;
+            for (int32_t j = 0; j < k; ++j) {
+                w[j] = exp((double)row[idx[j]] - m);
+                sum += w[j];
+            }
+            for (int32_t j = 0; j < k; ++j)
+                w[j] /= sum;
+        } else {
+            double m = -INFINITY;
+            for (int32_t e = 0; e < E; ++e)
+                if ((double)row[e] > m)
+                    m = (double)row[e];
+            double sum = 0.0;
+            for (int32_t e = 0; e < E; ++e)
+                sum += exp((double)row[e] - m);
+            for (int32_t j = 0; j < k; ++j)
+                w[j] = exp((double)row[idx[j]] - m) / sum;
+        }
+    }
+    free(s);
+    free(taken);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* dispatch layout: counts, offsets, capacity drops, positions         */
+/* ------------------------------------------------------------------ */
+
+/*
+ * Experts are placed on destinations in contiguous blocks of E/R.
+ * demand[e]  = number of (t, j) with topk_idx[t][j] == e.
+ * Walking t = 0..T-1 and j = 0..k-1 in order, the assignment (t, j) to
+ * expert e is kept iff capacity < 0 (dropless) or fewer than `capacity`
+ * earlier assignments to e were kept; its rank is that number.
+ * counts[e]  = kept assignments of e = min(demand[e], capacity).
+ * expert_offsets = exclusive running sum of counts (E + 1 entries).
+ * dest_counts[r] = sum of counts over r's experts;
+ * dest_offsets[r] = expert_offsets[r * E/R], dest_offsets[R] = N.
+ * pos[t][j] = expert_offsets[e] + rank, or -1 when dropped;
+ * send_src[pos] = t for every kept assignment (may be NULL).
+ * The send rows are therefore grouped by destination, by expert inside a
+ * destination and by token inside an expert.
+ * Returns 0, or -1 on bad sizes or an expert id outside [0, E).
+ */
+int oracle_dispatch_layout(const int32_t *topk_idx, int64_t T, int32_t E,
+                           int32_t k, int32_t R, int32_t capacity,
+                           int32_t *demand, int32_t *counts,
+                           int32_t *expert_offsets, int32_t *dest_counts,
+                           int32_t *dest_offsets, int32_t *pos,
+                           int32_t *send_src)
+{
+    if (T < 0 || E <= 0 || k <= 0 || R <= 0 || E % R != 0)
+        return -1;
+    int64_t n = T * (int64_t)k;
+    for (int64_t a = 0; a < n; ++a)
+        if (topk_idx[a] < 0 || topk_idx[a] >= E)
+            return -1;
+
+    for (int32_t e = 0; e < E; ++e)
+        demand[e] = 0;
+    for (int64_t a = 0; a < n; ++a)
+        demand[topk_idx[a]] += 1;
+
+    for (int32_t e = 0; e < E; ++e)
+        counts[e] = (capacity < 0 || demand[e] < capacity) ? demand[e] : capacity;
+
+    expert_offsets[0] = 0;
+    for (int32_t e = 0; e < E; ++e)
+        expert_offsets[e + 1] = expert_offsets[e] + counts[e];
+
+    int32_t el = E / R;
+    for (int32_t r = 0; r < R; ++r) {
+        dest_counts[r] = 0;
+        for (int32_t e = r * el; e < (r + 1) * el; ++e)
+            dest_counts[r] += counts[e];
+        dest_offsets[r] = expert_offsets[r * el];
+    }
+    dest_offsets[R] = expert_offsets[E];
+
+    int32_t *seen = (int32_t *)calloc((size_t)E, sizeof(int32_t));
+    if (!seen)
+        return -1;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < k; ++j) {
+            int64_t a = t * k + j;
+            int32_t e = topk_idx[a];
+            if (capacity >= 0 && seen[e] >= capacity) {
+                pos[a] = -1;
+                continue;
+            }
+            int32_t rank = seen[e]++;
+            pos[a] = expert_offsets[e] + rank;
+            if (send_src)
+                send_src[pos[a]] = (int32_t)t;
+        }
+    }
+    free(seen);
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* dispatch permute: pack each kept replica into its send row          */
+/* ------------------------------------------------------------------ */
+
+/*
+ * send[pos[t][j]][:] = x[t][:] for every kept (t, j): a bit copy of the bf16
+ * row. Rows no assignment points at are left as they were.
+ * Returns 0, or -1 when a position falls outside [0, send_rows).
+ */
+int oracle_dispatch_permute(const uint16_t *x, const int32_t *pos, int64_t T,
+                            int32_t H, int32_t k, uint16_t *send,
+                            int64_t send_rows)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t p = pos[t * k + j];
+            if (p < 0)
+                continue;
+            if (p >= send_rows)
+                return -1;
+            for (int32_t h = 0; h < H; ++h)
+                send[(int64_t)p * H + h] = x[t * (int64_t)H + h];
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* combine: inverse permutation, gate-weighted sum, shared, residual   */
+/* ------------------------------------------------------------------ */
+
+/*
+ * For each listed token t (all tokens when `tokens` is NULL; row i of `out`
+ * belongs to tokens[i]) and each h:
+ *   out = sum over kept j of w[t][j] * y[pos[t][j]][h]
+ *       + shared[t][h]      (when shared is given; weight 1)
+ *       + residual[t][h]    (when residual is given)
+ * in double precision. A dropped replica (pos < 0) contributes nothing and
+ * the remaining weights are not renormalised.
+ * Returns 0, or -1 when a position falls outside [0, y_rows).
+ */
+int oracle_combine_reduce(const uint16_t *y, int64_t y_rows, const int32_t *pos,
+                          const double *w, const uint16_t *shared,
+                          const uint16_t *residual, int64_t T, int32_t H,
+                          int32_t k, const int64_t *tokens, int64_t n_tokens,
+                          double *out)
+{
+    int64_t rows = tokens ? n_tokens : T;
+    for (int64_t i = 0; i < rows; ++i) {
+        int64_t t = tokens ? tokens[i] : i;
+        if (t < 0 || t >= T)
+            return -1;
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t p = pos[t * k + j];
+            if (p >= y_rows)
+                return -1;
+        }
+        for (int32_t h = 0; h < H; ++h) {
+            double acc = 0.0;
+            for (int32_t j = 0; j < k; ++j) {
+                int32_t p = pos[t * k + j];
+                if (p < 0)
+                    continue;
+                acc += w[t * k + j] * bf16_value(y[(int64_t)p * H + h]);
+            }
+            if (shared)
+                acc += bf16_value(shared[t * (int64_t)H + h]);
+            if (residual)
+                acc += bf16_value(residual[t * (int64_t)H + h]);
+            out[i * (int64_t)H + h] = acc;
+        }
+    }
+    return 0;
+}

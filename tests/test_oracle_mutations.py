@@ -1,0 +1,55 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case plants one mistake in a copy of oracle.c (a flipped tie-break, a
+dropped term, an off-by-one, a wrong index), builds it with gcc and runs the
+oracle pin tests against it in a subprocess; every variant must fail them.
+"""
+
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "oracle.c")
+PIN_TESTS = ["tests/test_oracle_route.py", "tests/test_oracle_layout.py", "tests/test_oracle_combine.py"]
+
+MUTATIONS = {
+    "tie_break_to_higher_id": ("    return ia < ib;\n", "    return ia > ib;\n"),
+    "nan_ranks_on_top": ("    if (!na && nb)\n        return 1;", "    if (!na && nb)\n        return 0;"),
+    "weights_from_biased_scores": ("                w[j] = exp((double)row[idx[j]] - m);",
+                                   "                w[j] = exp((double)s[idx[j]] - m);"),
+    "weights_not_normalised": ("                w[j] /= sum;", "                w[j] /= 1.0;"),
+    "score_ignores_bias": ("s[e] = bias ? row[e] + bias[e] : row[e];", "s[e] = row[e];"),
+    "capacity_off_by_one": ("if (capacity >= 0 && seen[e] >= capacity)", "if (capacity >= 0 && seen[e] > capacity)"),
+    "offsets_from_demand": ("expert_offsets[e] + counts[e];", "expert_offsets[e] + demand[e];"),
+    "dest_offset_wrong_index": ("dest_offsets[r] = expert_offsets[r * el];", "dest_offsets[r] = expert_offsets[r];"),
+    "permute_reversed_row": ("send[(int64_t)p * H + h] = x[t * (int64_t)H + h];",
+                             "send[(int64_t)p * H + h] = x[t * (int64_t)H + (H - 1 - h)];"),
+    "combine_drops_residual": ("acc += bf16_value(residual[t * (int64_t)H + h]);",
+                               "acc += 0.0 * bf16_value(residual[t * (int64_t)H + h]);"),
+    "combine_half_shared": ("acc += bf16_value(shared[t * (int64_t)H + h]);",
+                            "acc += 0.5 * bf16_value(shared[t * (int64_t)H + h]);"),
+    "combine_weight_index_reversed": ("acc += w[t * k + j] *", "acc += w[t * k + (k - 1 - j)] *"),
+    "combine_keeps_dropped_term": ("                if (p < 0)\n                    continue;\n                acc",
+                                   "                if (p < 0)\n                    p = 0;\n                acc"),
+    "bf16_ties_away_from_zero": ("double r = nearbyint(a / q) * q;", "double r = round(a / q) * q;"),
+    "bf16_no_subnormal_spacing": ("if (e < -126)\n        e = -126;", "if (e < -140)\n        e = -140;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_pins_catch_mutation(name, tmp_path):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not unique/found"
+    mutated = tmp_path / "oracle_mut.c"
+    mutated.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mut.so"
+    subprocess.run(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-shared",
+                    "-fPIC", str(mutated), "-o", str(lib), "-lm"], check=True)
+    env = dict(os.environ, ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider", *PIN_TESTS],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=300)
+    assert r.returncode != 0, f"mutation {name} survived the pins:\n{r.stdout[-2000:]}"
