@@ -1,0 +1,287 @@
+"""Benchmark of the MoE dispatch/combine core on one MI355X.
+
+One step = the whole path over one synthetic batch already resident in HBM:
+moe_route_topk -> moe_dispatch_layout -> moe_dispatch_permute ->
+moe_combine_reduce (the expert is the identity: combine reads the send
+buffer). W untimed warm-up steps, then exactly K timed steps between
+device synchronisations, with HIP events around every call on the stream the
+kernels run on.
+
+Prints ONE JSON line on stdout. `value` is algorithmic HBM bytes per step /
+step time (GB/s); tokens/s and the fraction of the 8 TB/s peak ride along.
+Algorithmic bytes count every array each call must read once and write once,
+for kept rows only:
+  route    T*E*4 (+E*4 bias) + 2*T*k*4
+  layout   2*T*k*4 + N*4 + (3E + 2R + 2)*4
+  permute  T*k*4 + T_read*H*2 + N*H*2
+  combine  2*T*k*4 + N*H*2 + T*H*2*(residual + shared) + T*H*2
+with N kept rows and T_read tokens that have at least one kept replica (both
+read from the path's own outputs after the timed region).
+
+The CPU-baseline leg times the plain C oracle on the same host arrays.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import synthetic  # noqa: E402
+
+HBM_PEAK_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = {
+    "combine_kernel": "combine_route_topk_amd/csrc/combine.hip",
+    "permute_kernel": "combine_route_topk_amd/csrc/permute.hip",
+}
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", default="fine_grained",
+                   help="one of " + ", ".join(w.name for w in synthetic.WORKLOADS.values()))
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0,
+                   help="rough CPU time budget of the oracle baseline")
+    p.add_argument("--copy-probe-mib", type=int, default=0,
+                   help="also run a plain copy kernel of this size (for counter calibration)")
+    return p.parse_args()
+
+
+def workload_by_name(name):
+    for i, w in synthetic.WORKLOADS.items():
+        if name in (w.name, str(i)):
+            return w
+    raise SystemExit(f"unknown workload {name}")
+
+
+def algorithmic_bytes(w, N, T_read, has_bias):
+    T, H, E, k, R = w.T, w.H, w.E, w.k, w.R
+    dense = 1 + (1 if w.residual else 0) + (1 if w.shared else 0)   # out + residual + shared
+    return {
+        "route": T * E * 4 + (E * 4 if has_bias else 0) + 2 * T * k * 4,
+        "layout": 2 * T * k * 4 + N * 4 + (3 * E + 2 * R + 2) * 4,
+        "permute": T * k * 4 + T_read * H * 2 + N * H * 2,
+        "combine": 2 * T * k * 4 + N * H * 2 + T * H * 2 * dense,
+    }
+
+
+def source_hash(rel):
+    with open(os.path.join(ROOT, rel), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def stored_traffic(kernel, workload):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
+    absent or taken on a different version of the kernel's source."""
+    path = os.path.join(PROFILES, f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, d, budget_s):
+    """Time the single-threaded C oracle over the same workload."""
+    import oracle
+    reps, times = 0, []
+    t_start = time.perf_counter()
+    while True:
+        t0 = time.perf_counter()
+        idx, wt = oracle.route_topk(d["logits"], d["bias"], w.k)
+        L = oracle.dispatch_layout(idx, w.E, w.R, w.capacity)
+        N = int(L["expert_offsets"][-1])
+        send = oracle.dispatch_permute(d["x"], L["pos"], max(N, 1))
+        oracle.combine_reduce(send, L["pos"], wt, d["shared"], d["residual"])
+        times.append(time.perf_counter() - t0)
+        reps += 1
+        del send
+        if reps >= 5 or time.perf_counter() - t_start > budget_s:
+            break
+    return statistics.median(times), reps
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this path has no inter-GPU exchange "
+              "(the R destinations are partitions of one HBM buffer); run with --gpus 1",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import combine_route_topk_amd as moe
+
+    w = workload_by_name(args.workload)
+    log("workload", w.describe())
+    t0 = time.perf_counter()
+    d = synthetic.make_inputs(w, seed=0)
+    log(f"inputs generated in {time.perf_counter() - t0:.1f}s")
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(a, bf16=False):
+        if a is None:
+            return None
+        t = torch.from_numpy(np.ascontiguousarray(a))
+        return (t.view(torch.bfloat16) if bf16 else t).to(dev)
+
+    logits, bias = up(d["logits"]), up(d["bias"])
+    x, res, sh = up(d["x"], True), up(d["residual"], True), up(d["shared"], True)
+    T, H, E, k, R, C = w.T, w.H, w.E, w.k, w.R, w.capacity
+    send_rows = T * k if C < 0 else min(T * k, E * C)
+    i32 = dict(dtype=torch.int32, device=dev)
+    idx = torch.empty((T, k), **i32)
+    wt = torch.empty((T, k), dtype=torch.float32, device=dev)
+    lay = {"expert_demand": torch.empty(E, **i32), "expert_counts": torch.empty(E, **i32),
+           "expert_offsets": torch.empty(E + 1, **i32), "dest_counts": torch.empty(R, **i32),
+           "dest_offsets": torch.empty(R + 1, **i32), "pos": torch.empty((T, k), **i32),
+           "send_src": torch.empty(T * k, **i32)}
+    ws = torch.empty(max(moe.moe_layout_workspace_size(T, E, k, R), 16), dtype=torch.uint8, device=dev)
+    send = torch.empty((send_rows, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+    sp = stream.cuda_stream
+    lib = moe.lib
+    P = lambda t: None if t is None else t.data_ptr()
+
+    def check(name, rc):
+        if rc != moe.MOE_OK:
+            raise RuntimeError(f"{name}: {moe.moe_status_string(rc)}")
+
+    calls = [
+        ("route", lambda: check("route", lib.moe_route_topk(
+            P(logits), P(bias), T, E, k, moe.MOE_ROUTE_NORMALIZE, P(idx), P(wt), sp))),
+        ("layout", lambda: check("layout", lib.moe_dispatch_layout(
+            P(idx), T, E, k, R, C, P(lay["expert_demand"]), P(lay["expert_counts"]),
+            P(lay["expert_offsets"]), P(lay["dest_counts"]), P(lay["dest_offsets"]),
+            P(lay["pos"]), P(lay["send_src"]), P(ws), ws.numel(), sp))),
+        ("permute", lambda: check("permute", lib.moe_dispatch_permute(
+            P(x), P(lay["pos"]), T, H, k, P(send), send_rows, sp))),
+        ("combine", lambda: check("combine", lib.moe_combine_reduce(
+            P(send), send_rows, P(lay["pos"]), P(wt), P(sh), P(res), T, H, k, 0, P(out), sp))),
+    ]
+
+    def step(evs=None):
+        for i, (_, fn) in enumerate(calls):
+            if evs is not None:
+                evs[i].record(stream)
+            fn()
+        if evs is not None:
+            evs[len(calls)].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log(f"warmup {args.warmup} steps done")
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    gpu_ms = ev[0][0].elapsed_time(ev[-1][-1])
+    per_call_ms = {name: statistics.mean(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(args.steps))
+                   for i, (name, _) in enumerate(calls)}
+    ms_per_step = gpu_ms / args.steps
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall_s / args.steps * 1e6:.1f} us/step)")
+    log("per call (us): " + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in per_call_ms.items()))
+
+    # bookkeeping from the path's own outputs (outside the timed region)
+    N = int(lay["expert_offsets"][E].item())
+    T_read = int((lay["pos"] >= 0).any(dim=1).sum().item())
+    nbytes = algorithmic_bytes(w, N, T_read, bias is not None)
+    total = sum(nbytes.values())
+    gbps = total / (ms_per_step * 1e-3) / 1e9
+    tokens_per_s = T / (ms_per_step * 1e-3)
+
+    dominant = max(("permute", "combine"), key=lambda n: per_call_ms[n])
+    kname = f"{dominant}_kernel"
+    achieved = nbytes[dominant] / (per_call_ms[dominant] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(kname, w.name),
+                "kernel": kname, "algorithmic_bytes": nbytes[dominant],
+                "avg_launch_us": round(per_call_ms[dominant] * 1e3, 2)}
+
+    copy_probe = None
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 2
+        a = torch.randn(n, device=dev).to(torch.bfloat16)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            torch.neg(a, out=b)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(10):
+            torch.neg(a, out=b)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / 10
+        copy_probe = {"bytes_per_launch": 2 * a.numel() * 2, "avg_launch_us": round(ms * 1e3, 2),
+                      "GBps": round(2 * a.numel() * 2 / (ms * 1e-3) / 1e9, 1)}
+        log("copy probe", copy_probe)
+
+    result = {
+        "metric": "dispatch+combine HBM GB/s (% of MI355X peak) and tokens/s, 1 GPU",
+        "value": round(gbps, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.describe(), "T": T, "H": H, "E": E, "k": k, "R": R,
+                   "capacity": C, "shared_expert": w.shared, "kept_rows": N, "tokens_read": T_read,
+                   "bytes_per_step": total, "parallelism": "single GPU (R logical destinations)"},
+        "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "tokens_per_s": round(tokens_per_s, 1),
+        "per_call_us": {n: round(v * 1e3, 2) for n, v in per_call_ms.items()},
+        "per_call_GBps": {n: round(nbytes[n] / (per_call_ms[n] * 1e-3) / 1e9, 1) for n in nbytes},
+        "roofline": roofline,
+    }
+    if copy_probe:
+        result["copy_probe"] = copy_probe
+
+    if not args.no_cpu_baseline:
+        log("cpu baseline: timing the C oracle on the same host arrays")
+        sec, reps = cpu_baseline(w, d, args.cpu_seconds)
+        result["cpu_baseline"] = {
+            "value": round(total / sec / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"the full {w.name} batch (T={T}), {reps} rep(s), median {sec:.2f}s per pass; "
+                      f"single-threaded C oracle on {platform.processor() or platform.machine()}",
+            "tokens_per_s": round(T / sec, 1),
+        }
+        log("cpu baseline", result["cpu_baseline"])
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,189 @@
+"""Thin Python binding of libmoe_ep.so, the MI355X MoE dispatch/combine core.
+
+The functions carry the names of the C entry points declared in
+include/moe_ep.h and only marshal arguments: they check that tensors live
+on the GPU with the dtype and contiguity the ABI expects, allocate missing
+outputs with torch (PyTorch is used for device memory and streams only),
+and pass raw pointers plus the current HIP stream to the library. Every
+step of the path runs in the library's HIP kernels; there is no fallback.
+Importing this package fails when the library has not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libmoe_ep.so")
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE = 3
+MOE_ERR_LAUNCH = 4
+MOE_ROUTE_NORMALIZE = 1
+MOE_COMBINE_OUT_FP32 = 1
+
+EXPORTS = ("moe_route_topk", "moe_layout_workspace_size", "moe_dispatch_layout",
+           "moe_dispatch_permute", "moe_combine_reduce", "moe_status_string")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {moe_status_string(status)}")
+        self.status = status
+
+
+def _load_library() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built; build it with `python combine_route_topk_amd/build.py` "
+            "(hipcc, gfx950) before using the package")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
+    lib.moe_route_topk.argtypes = [P, P, i64, i32, i32, u32, P, P, P]
+    lib.moe_layout_workspace_size.argtypes = [i64, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_dispatch_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P,
+                                        ctypes.c_size_t, P]
+    lib.moe_dispatch_permute.argtypes = [P, P, i64, i32, i32, P, i64, P]
+    lib.moe_combine_reduce.argtypes = [P, i64, P, P, P, P, i64, i32, i32, u32, P, P]
+    lib.moe_status_string.argtypes = [ctypes.c_int]
+    lib.moe_status_string.restype = ctypes.c_char_p
+    for name in EXPORTS[:-1]:
+        getattr(lib, name).restype = ctypes.c_int
+    return lib
+
+
+lib = _load_library()
+
+
+def moe_status_string(status: int) -> str:
+    return lib.moe_status_string(int(status)).decode()
+
+
+def _check(fn: str, status: int):
+    if status != MOE_OK:
+        raise MoeError(fn, status)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else stream
+
+
+def _ptr(t: Optional[torch.Tensor], dtypes, name: str, ndim: Optional[int] = None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions")
+    return t.data_ptr() or None
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+
+
+def moe_route_topk(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int,
+                   normalize: bool = True, topk_idx: Optional[torch.Tensor] = None,
+                   topk_w: Optional[torch.Tensor] = None, stream=None):
+    """Top-k experts per token and their gate weights (see moe_route_topk)."""
+    T, E = logits.shape
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check("moe_route_topk", lib.moe_route_topk(
+        _ptr(logits, _F32, "logits", 2), _ptr(bias, _F32, "bias", 1), T, E, k,
+        MOE_ROUTE_NORMALIZE if normalize else 0, _ptr(topk_idx, _I32, "topk_idx"),
+        _ptr(topk_w, _F32, "topk_w"), _stream(stream)))
+    return topk_idx, topk_w
+
+
+def moe_layout_workspace_size(T: int, E: int, k: int, R: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_layout_workspace_size", lib.moe_layout_workspace_size(T, E, k, R, ctypes.byref(n)))
+    return n.value
+
+
+def moe_dispatch_layout(topk_idx: torch.Tensor, E: int, R: int, capacity: int = -1,
+                        workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None,
+                        with_send_src: bool = True, stream=None) -> dict:
+    """Counts, offsets, drops and send positions (see moe_dispatch_layout).
+
+    Returns a dict of int32 GPU tensors: expert_demand [E], expert_counts [E],
+    expert_offsets [E+1], dest_counts [R], dest_offsets [R+1], pos [T,k] and
+    send_src [T*k] (or None). `out` may hold preallocated tensors by name.
+    """
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    o = dict(out or {})
+
+    def get(name, shape):
+        if o.get(name) is None:
+            o[name] = torch.empty(shape, dtype=torch.int32, device=dev)
+        return o[name]
+
+    get("expert_demand", (E,)); get("expert_counts", (E,)); get("expert_offsets", (E + 1,))
+    get("dest_counts", (R,)); get("dest_offsets", (R + 1,)); get("pos", (T, k))
+    if with_send_src:
+        get("send_src", (T * k,))
+    else:
+        o["send_src"] = None
+    need = moe_layout_workspace_size(T, E, k, R)
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=dev)
+    _check("moe_dispatch_layout", lib.moe_dispatch_layout(
+        _ptr(topk_idx, _I32, "topk_idx", 2), T, E, k, R, capacity,
+        _ptr(o["expert_demand"], _I32, "expert_demand"), _ptr(o["expert_counts"], _I32, "expert_counts"),
+        _ptr(o["expert_offsets"], _I32, "expert_offsets"), _ptr(o["dest_counts"], _I32, "dest_counts"),
+        _ptr(o["dest_offsets"], _I32, "dest_offsets"), _ptr(o["pos"], _I32, "pos"),
+        _ptr(o["send_src"], _I32, "send_src"), _ptr(workspace, (torch.uint8,), "workspace"),
+        workspace.numel(), _stream(stream)))
+    return o
+
+
+def moe_dispatch_permute(x: torch.Tensor, pos: torch.Tensor, send_rows: int,
+                         send: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """send[pos[t, j]] = x[t] for every kept replica (see moe_dispatch_permute)."""
+    T, H = x.shape
+    k = pos.shape[1]
+    if send is None:
+        send = torch.empty((send_rows, H), dtype=x.dtype, device=x.device)
+    if send.shape[0] < send_rows or (send.dim() == 2 and send.shape[1] != H):
+        raise ValueError("send buffer smaller than send_rows x H")
+    _check("moe_dispatch_permute", lib.moe_dispatch_permute(
+        _ptr(x, _BF16, "x", 2), _ptr(pos, _I32, "pos", 2), T, H, k,
+        _ptr(send, _BF16, "send"), send_rows, _stream(stream)))
+    return send
+
+
+def moe_combine_reduce(y: torch.Tensor, pos: torch.Tensor, topk_w: torch.Tensor,
+                       shared: Optional[torch.Tensor] = None,
+                       residual: Optional[torch.Tensor] = None, out_fp32: bool = False,
+                       out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """Gate-weighted sum of the kept expert rows + shared + residual
+    (see moe_combine_reduce). Returns bf16 [T, H], or float32 with out_fp32."""
+    T, k = pos.shape
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32 if out_fp32 else torch.bfloat16,
+                          device=pos.device)
+    want = _F32 if out_fp32 else _BF16
+    _check("moe_combine_reduce", lib.moe_combine_reduce(
+        _ptr(y, _BF16, "y", 2), y.shape[0], _ptr(pos, _I32, "pos", 2),
+        _ptr(topk_w, _F32, "topk_w"), _ptr(shared, _BF16, "shared", 2),
+        _ptr(residual, _BF16, "residual", 2), T, H, k,
+        MOE_COMBINE_OUT_FP32 if out_fp32 else 0, _ptr(out, want, "out"), _stream(stream)))
+    return out

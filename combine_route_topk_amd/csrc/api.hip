@@ -1,0 +1,182 @@
+// api.hip -- the C ABI declared in include/moe_ep.h: argument validation on
+// the host, then one launcher call on the caller's stream. Nothing here
+// touches the GPU before every check has passed.
+#include "moe_ep.h"
+
+#include "launch.hpp"
+
+namespace {
+
+constexpr int32_t kMaxE = 1024;
+constexpr int32_t kMaxK = 32;
+constexpr int32_t kMaxH = 65536;
+constexpr int64_t kMaxAssignments = (int64_t)1 << 31;
+
+bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+// k and the token count: shared by every entry point.
+moe_status_t check_tokens(int64_t T, int32_t k)
+{
+    if (T < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (k < 1 || k > kMaxK)
+        return MOE_ERR_UNSUPPORTED;
+    if (T * (int64_t)k >= kMaxAssignments)
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status_t check_experts(int32_t E, int32_t k)
+{
+    if (E < 1 || E > kMaxE || k > E)
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status_t check_hidden(int32_t H)
+{
+    if (H <= 0 || H % 8 != 0 || H > kMaxH)
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status_t check_layout_sizes(int64_t T, int32_t E, int32_t k, int32_t R)
+{
+    moe_status_t s = check_tokens(T, k);
+    if (s != MOE_OK)
+        return s;
+    if ((s = check_experts(E, k)) != MOE_OK)
+        return s;
+    if (R < 1 || E % R != 0)
+        return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+moe_status_t from_hip(hipError_t err) { return err == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+moe_status_t moe_route_topk(const float *logits, const float *bias, int64_t T, int32_t E,
+                            int32_t k, uint32_t flags, int32_t *topk_idx, float *topk_w,
+                            void *stream)
+{
+    moe_status_t s = check_tokens(T, k);
+    if (s != MOE_OK)
+        return s;
+    if ((s = check_experts(E, k)) != MOE_OK)
+        return s;
+    if (flags & ~MOE_ROUTE_NORMALIZE)
+        return MOE_ERR_INVALID_ARG;
+    if (T == 0)
+        return MOE_OK;
+    if (!logits || !topk_idx || !topk_w)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(logits, 4) || !aligned(bias, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4))
+        return MOE_ERR_INVALID_ARG;
+    return from_hip(moe::launch_route_topk(logits, bias, T, E, k,
+                                           (flags & MOE_ROUTE_NORMALIZE) != 0, topk_idx, topk_w,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_layout_workspace_size(int64_t T, int32_t E, int32_t k, int32_t R, size_t *bytes)
+{
+    if (!bytes)
+        return MOE_ERR_INVALID_ARG;
+    moe_status_t s = check_layout_sizes(T, E, k, R);
+    if (s != MOE_OK)
+        return s;
+    *bytes = moe::layout_workspace_bytes(T * (int64_t)k, E);
+    return MOE_OK;
+}
+
+moe_status_t moe_dispatch_layout(const int32_t *topk_idx, int64_t T, int32_t E, int32_t k,
+                                 int32_t R, int32_t capacity, int32_t *expert_demand,
+                                 int32_t *expert_counts, int32_t *expert_offsets,
+                                 int32_t *dest_counts, int32_t *dest_offsets, int32_t *pos,
+                                 int32_t *send_src, void *workspace, size_t workspace_bytes,
+                                 void *stream)
+{
+    moe_status_t s = check_layout_sizes(T, E, k, R);
+    if (s != MOE_OK)
+        return s;
+    if ((T > 0 && (!topk_idx || !pos)) || !expert_demand || !expert_counts || !expert_offsets ||
+        !dest_counts || !dest_offsets)
+        return MOE_ERR_INVALID_ARG;
+    const void *ptrs[] = {topk_idx,     expert_demand, expert_counts, expert_offsets,
+                          dest_counts, dest_offsets,  pos,           send_src};
+    for (const void *p : ptrs)
+        if (!aligned(p, 4))
+            return MOE_ERR_INVALID_ARG;
+    const size_t need = moe::layout_workspace_bytes(T * (int64_t)k, E);
+    if (need > 0 && (!workspace || workspace_bytes < need || !aligned(workspace, 16)))
+        return MOE_ERR_WORKSPACE;
+    return from_hip(moe::launch_dispatch_layout(
+        topk_idx, T, E, k, R, capacity, expert_demand, expert_counts, expert_offsets, dest_counts,
+        dest_offsets, pos, send_src, static_cast<int32_t *>(workspace),
+        static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_dispatch_permute(const uint16_t *x, const int32_t *pos, int64_t T, int32_t H,
+                                  int32_t k, uint16_t *send, int64_t send_rows, void *stream)
+{
+    moe_status_t s = check_tokens(T, k);
+    if (s != MOE_OK)
+        return s;
+    if ((s = check_hidden(H)) != MOE_OK)
+        return s;
+    if (send_rows < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (T == 0)
+        return MOE_OK;
+    if (!x || !pos || (!send && send_rows > 0))
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(send, 16) || !aligned(pos, 4))
+        return MOE_ERR_INVALID_ARG;
+    return from_hip(moe::launch_dispatch_permute(x, pos, T, H, k, send, send_rows,
+                                                 static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_combine_reduce(const uint16_t *y, int64_t y_rows, const int32_t *pos,
+                                const float *topk_w, const uint16_t *shared,
+                                const uint16_t *residual, int64_t T, int32_t H, int32_t k,
+                                uint32_t flags, void *out, void *stream)
+{
+    moe_status_t s = check_tokens(T, k);
+    if (s != MOE_OK)
+        return s;
+    if ((s = check_hidden(H)) != MOE_OK)
+        return s;
+    if (y_rows < 0 || (flags & ~MOE_COMBINE_OUT_FP32))
+        return MOE_ERR_INVALID_ARG;
+    if (T == 0)
+        return MOE_OK;
+    if (!pos || !topk_w || !out || (!y && y_rows > 0))
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(y, 16) || !aligned(shared, 16) || !aligned(residual, 16) || !aligned(out, 16) ||
+        !aligned(pos, 4) || !aligned(topk_w, 4))
+        return MOE_ERR_INVALID_ARG;
+    return from_hip(moe::launch_combine_reduce(y, y_rows, pos, topk_w, shared, residual, T, H, k,
+                                               (flags & MOE_COMBINE_OUT_FP32) != 0, out,
+                                               static_cast<hipStream_t>(stream)));
+}
+
+const char *moe_status_string(moe_status_t status)
+{
+    switch (status) {
+    case MOE_OK:
+        return "MOE_OK";
+    case MOE_ERR_INVALID_ARG:
+        return "MOE_ERR_INVALID_ARG: invalid argument";
+    case MOE_ERR_UNSUPPORTED:
+        return "MOE_ERR_UNSUPPORTED: size outside the supported limits";
+    case MOE_ERR_WORKSPACE:
+        return "MOE_ERR_WORKSPACE: workspace missing or too small";
+    case MOE_ERR_LAUNCH:
+        return "MOE_ERR_LAUNCH: kernel launch failed";
+    }
+    return "unknown moe_status_t";
+}
+
+}  // extern "C"

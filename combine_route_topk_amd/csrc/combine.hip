@@ -1,0 +1,145 @@
+// combine.hip -- inverse permutation and gate-weighted reduction at the
+// token's origin, plus the shared expert and the residual.
+//
+// Method: aicassindra "gpu_moe_all_to_all", "Two collectives per layer"
+// (expert outputs come back along the inverse permutation, k partial results
+// per token, scaled by the router's gate weights); "MoE All-to-All Dispatch
+// and Ragged Routing", "Returning Tokens to the Original GPU" (the residual
+// add happens where x lives); ai-from-scratch "19. All-to-all", section on
+// 512 experts (an always-active shared expert next to the routed ones).
+//
+// Block (t, y) produces a 4 KiB column slab of out[t]: each lane owns 8
+// consecutive elements. The kept rows' positions and weights are uniform
+// per block (scalar loads); all k 16-byte row loads are issued before the
+// first multiply so that k loads per lane are in flight. Accumulation is
+// float32, one fused multiply-add per kept replica in ascending j, then
+// + shared, then + residual, then a single rounding (gfx950's packed
+// round-to-nearest-even bf16 convert) or a float32 store.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kRowThreads = 256;
+
+__device__ __forceinline__ void add_bf16x8(float (&acc)[8], const u32x4 &v)
+{
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        acc[2 * q] += bf16_lo(v[q]);
+        acc[2 * q + 1] += bf16_hi(v[q]);
+    }
+}
+
+template <int KMAX, bool OUT_F32>
+__global__ __launch_bounds__(kRowThreads) void combine_kernel(
+    const u32x4 *__restrict__ y, int64_t y_rows, const int32_t *__restrict__ pos,
+    const float *__restrict__ topk_w, const u32x4 *__restrict__ shared,
+    const u32x4 *__restrict__ residual, int32_t C16, int32_t k, void *__restrict__ out)
+{
+    const int64_t t = blockIdx.x;
+    const int32_t c = blockIdx.y * kRowThreads + threadIdx.x;
+    if (c >= C16)
+        return;
+    int32_t p[KMAX];
+    float wt[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        p[j] = -1;
+        wt[j] = 0.f;
+        if (j < k) {
+            const int32_t q = pos[t * k + j];
+            if (q >= 0 && q < y_rows) {
+                p[j] = q;
+                wt[j] = topk_w[t * k + j];
+            }
+        }
+    }
+    u32x4 v[KMAX];
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j)
+        if (p[j] >= 0)
+            v[j] = load_stream(y + (int64_t)p[j] * C16 + c);
+    u32x4 sv = {0u, 0u, 0u, 0u}, rv = {0u, 0u, 0u, 0u};
+    if (shared)
+        sv = load_stream(shared + t * C16 + c);
+    if (residual)
+        rv = load_stream(residual + t * C16 + c);
+
+    float acc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        acc[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < KMAX; ++j) {
+        if (p[j] >= 0) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                acc[2 * q] = fmaf(wt[j], bf16_lo(v[j][q]), acc[2 * q]);
+                acc[2 * q + 1] = fmaf(wt[j], bf16_hi(v[j][q]), acc[2 * q + 1]);
+            }
+        }
+    }
+    if (shared)
+        add_bf16x8(acc, sv);
+    if (residual)
+        add_bf16x8(acc, rv);
+
+    if (OUT_F32) {
+        u32x4 *o = reinterpret_cast<u32x4 *>(out) + (t * C16 + c) * 2;
+        const u32x4 lo = {__float_as_uint(acc[0]), __float_as_uint(acc[1]),
+                          __float_as_uint(acc[2]), __float_as_uint(acc[3])};
+        const u32x4 hi = {__float_as_uint(acc[4]), __float_as_uint(acc[5]),
+                          __float_as_uint(acc[6]), __float_as_uint(acc[7])};
+        o[0] = lo;
+        o[1] = hi;
+    } else {
+        const u32x4 r = {pack_bf16x2(acc[0], acc[1]), pack_bf16x2(acc[2], acc[3]),
+                         pack_bf16x2(acc[4], acc[5]), pack_bf16x2(acc[6], acc[7])};
+        reinterpret_cast<u32x4 *>(out)[t * C16 + c] = r;
+    }
+}
+
+template <int KMAX>
+hipError_t launch_kmax(const uint16_t *y, int64_t y_rows, const int32_t *pos, const float *topk_w,
+                       const uint16_t *shared, const uint16_t *residual, int64_t T, int32_t H,
+                       int32_t k, bool out_fp32, void *out, hipStream_t stream)
+{
+    const int32_t C16 = H / 8;
+    const dim3 grid((unsigned)T, (unsigned)((C16 + kRowThreads - 1) / kRowThreads));
+    const u32x4 *yv = reinterpret_cast<const u32x4 *>(y);
+    const u32x4 *sv = reinterpret_cast<const u32x4 *>(shared);
+    const u32x4 *rv = reinterpret_cast<const u32x4 *>(residual);
+    if (out_fp32)
+        hipLaunchKernelGGL((combine_kernel<KMAX, true>), grid, dim3(kRowThreads), 0, stream, yv,
+                           y_rows, pos, topk_w, sv, rv, C16, k, out);
+    else
+        hipLaunchKernelGGL((combine_kernel<KMAX, false>), grid, dim3(kRowThreads), 0, stream, yv,
+                           y_rows, pos, topk_w, sv, rv, C16, k, out);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_combine_reduce(const uint16_t *y, int64_t y_rows, const int32_t *pos,
+                                 const float *topk_w, const uint16_t *shared,
+                                 const uint16_t *residual, int64_t T, int32_t H, int32_t k,
+                                 bool out_fp32, void *out, hipStream_t stream)
+{
+#define MOE_COMBINE_ARGS y, y_rows, pos, topk_w, shared, residual, T, H, k, out_fp32, out, stream
+    if (k <= 1)
+        return launch_kmax<1>(MOE_COMBINE_ARGS);
+    if (k <= 2)
+        return launch_kmax<2>(MOE_COMBINE_ARGS);
+    if (k <= 4)
+        return launch_kmax<4>(MOE_COMBINE_ARGS);
+    if (k <= 8)
+        return launch_kmax<8>(MOE_COMBINE_ARGS);
+    if (k <= 16)
+        return launch_kmax<16>(MOE_COMBINE_ARGS);
+    return launch_kmax<32>(MOE_COMBINE_ARGS);
+#undef MOE_COMBINE_ARGS
+}
+
+}  // namespace moe

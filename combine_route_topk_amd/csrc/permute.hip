@@ -1,0 +1,59 @@
+// permute.hip -- pack each kept replica of a token into its send row.
+//
+// Method: aicassindra "gpu_moe_all_to_all", "Bucketing" (make each
+// destination's rows contiguous, with the permutation fused into the kernel
+// that stages the sends) and "Two collectives per layer" (each token leaves
+// k times); thecoregrid "Mixture-of-experts acceleration through overlap",
+// paragraph on the remote-owner-aligned layout.
+//
+// Token-major scatter: block (t, y) reads a 4 KiB column slab of x[t] once,
+// 16 bytes per lane, and writes it to each of the token's kept send rows.
+// Row reads and writes are contiguous 16-byte-per-lane streams, so a wave
+// moves 1 KiB per instruction. Tokens whose replicas were all dropped
+// skip the read. Both streams carry the non-temporal hint: x is read once
+// and send is not read again by this kernel.
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kRowThreads = 256;
+
+__global__ __launch_bounds__(kRowThreads) void permute_kernel(
+    const u32x4 *__restrict__ x, const int32_t *__restrict__ pos, int32_t C16, int32_t k,
+    u32x4 *__restrict__ send, int64_t send_rows)
+{
+    const int64_t t = blockIdx.x;
+    const int32_t c = blockIdx.y * kRowThreads + threadIdx.x;
+    const int32_t *pr = pos + t * k;
+    bool any = false;
+    for (int j = 0; j < k; ++j) {
+        const int32_t p = pr[j];
+        any |= p >= 0 && p < send_rows;
+    }
+    if (!any || c >= C16)
+        return;
+    const u32x4 v = load_stream(x + t * C16 + c);
+    for (int j = 0; j < k; ++j) {
+        const int32_t p = pr[j];
+        if (p >= 0 && p < send_rows)
+            store_stream(send + (int64_t)p * C16 + c, v);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_dispatch_permute(const uint16_t *x, const int32_t *pos, int64_t T, int32_t H,
+                                   int32_t k, uint16_t *send, int64_t send_rows,
+                                   hipStream_t stream)
+{
+    const int32_t C16 = H / 8;
+    const dim3 grid((unsigned)T, (unsigned)((C16 + kRowThreads - 1) / kRowThreads));
+    hipLaunchKernelGGL(permute_kernel, grid, dim3(kRowThreads), 0, stream,
+                       reinterpret_cast<const u32x4 *>(x), pos, C16, k,
+                       reinterpret_cast<u32x4 *>(send), send_rows);
+    return hipGetLastError();
+}
+
+}  // namespace moe

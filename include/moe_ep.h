@@ -1,0 +1,224 @@
+/*
+ * moe_ep.h -- C ABI of the MoE expert-parallel dispatch/combine core, one
+ * rank's share, for AMD Instinct MI355X (gfx950).
+ *
+ * The library performs the data-parallel steps around the two all-to-all
+ * exchanges of an expert-parallel MoE layer: routing, the per-destination
+ * counts and offsets, packing each destination's rows contiguously, and
+ * the gate-weighted reduction when the expert outputs return. The R
+ * destinations are logical partitions of one device buffer; the library
+ * performs no inter-GPU transfer.
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller. The
+ *    library never allocates, frees or keeps a pointer after returning.
+ *  - Every call only enqueues work on `stream` (a hipStream_t passed as
+ *    void*; NULL is the null stream). No call synchronises the device or
+ *    reads device memory from the host, so routing results never make a
+ *    round trip through the host.
+ *  - bf16 tensors are passed as uint16_t bit patterns, row-major.
+ *  - Every scalar, required pointer and alignment is validated on the host
+ *    before anything is enqueued; on error nothing is enqueued, outputs are
+ *    untouched and the status says why. After a launch, a HIP launch error
+ *    is reported as MOE_ERR_LAUNCH. No exception crosses the ABI and there
+ *    is no global error state.
+ *  - T = 0 is legal: the call enqueues nothing, except moe_dispatch_layout,
+ *    which still writes its (all-zero) counts and offsets.
+ *  - Results are bitwise reproducible from run to run: no floating-point
+ *    atomics, integer atomics only where their order cannot matter.
+ *  - Limits: 1 <= k <= min(E, 32); 1 <= E <= 1024; E % R == 0; H % 8 == 0;
+ *    0 < H <= 65536; T * k < 2^31.
+ */
+#ifndef MOE_EP_H
+#define MOE_EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1,  /* NULL/misaligned pointer, bad size or relation */
+    MOE_ERR_UNSUPPORTED = 2,  /* outside the limits above */
+    MOE_ERR_WORKSPACE = 3,    /* workspace missing or too small */
+    MOE_ERR_LAUNCH = 4        /* the HIP runtime rejected a kernel launch */
+} moe_status_t;
+
+/* moe_route_topk flags */
+#define MOE_ROUTE_NORMALIZE 1u   /* weights renormalised over the k selected */
+
+/* moe_combine_reduce flags */
+#define MOE_COMBINE_OUT_FP32 1u  /* out is float[T][H] instead of bf16[T][H] */
+
+/*
+ * moe_route_topk -- pick k experts per token and their gate weights.
+ *
+ * Defined by: ai-from-scratch "19. All-to-all", intro (after attention every
+ * token holds a list of expert ids; results are mixed on return) and "Why
+ * the router can ruin your day" (a per-expert balancing bias takes part in
+ * the top-k decision only, never in the mix weights); aicassindra
+ * "gpu_moe_all_to_all", "Two collectives per layer, and what each one
+ * moves" (outputs are scaled by the router's gate weights).
+ *
+ * For each token t:
+ *   s[e] = logits[t][e] + bias[e]   (one float32 add; bias may be NULL)
+ *   topk_idx[t][0..k-1] = the k experts with the largest s, in descending
+ *     order; -0 equals +0; any NaN ranks below every number (including
+ *     -inf); ties go to the smaller expert id.
+ *   topk_w[t][j] from the UNBIASED logits l of the selected experts:
+ *     flags & MOE_ROUTE_NORMALIZE: w_j = exp(l_j - m) / sum_i exp(l_i - m)
+ *       over the k selected (m = their max); the weights sum to 1.
+ *     otherwise: w_j = exp(l_j - M) / sum over all E of exp(l_e - M)
+ *       (softmax over all experts, not renormalised).
+ *   Weights are computed in float32; for NaN or infinite logits they are
+ *   unspecified.
+ *
+ * Arguments:
+ *   logits   [T][E] float32, 4-byte aligned.
+ *   bias     [E] float32 or NULL (selection only).
+ *   topk_idx [T][k] int32 out;  topk_w [T][k] float32 out.
+ * Errors: MOE_ERR_INVALID_ARG for NULL/misaligned pointers or T < 0;
+ *   MOE_ERR_UNSUPPORTED outside the limits.
+ */
+moe_status_t moe_route_topk(const float *logits, const float *bias,
+                            int64_t T, int32_t E, int32_t k, uint32_t flags,
+                            int32_t *topk_idx, float *topk_w, void *stream);
+
+/*
+ * moe_layout_workspace_size -- bytes of device workspace that
+ * moe_dispatch_layout needs for these sizes (written to *bytes). The
+ * workspace needs no initialisation: the layout call clears what it uses,
+ * on-stream.
+ * Errors: as moe_dispatch_layout's size checks; *bytes untouched on error.
+ */
+moe_status_t moe_layout_workspace_size(int64_t T, int32_t E, int32_t k,
+                                       int32_t R, size_t *bytes);
+
+/*
+ * moe_dispatch_layout -- per-expert and per-destination counts, the offset
+ * table, capacity drops in token order, and every replica's send row.
+ *
+ * Defined by: aicassindra "gpu_moe_all_to_all", "Two collectives per layer"
+ * (per-destination counts precede the payload so that receivers can size
+ * their buffers) and "Bucketing: cut the message count, not the byte count"
+ * (sort by destination and build an offset table so that each destination
+ * is one contiguous segment; keep indices and counts on the device);
+ * "MoE All-to-All Dispatch and Ragged Routing", "Fixed Capacity vs. Ragged
+ * Routing" (per-sender-expert slots under a capacity factor, the excess
+ * dropped; ragged routing is dropless); ai-from-scratch "19. All-to-all",
+ * "Why the router can ruin your day" (a dropped token counts as having
+ * skipped that expert).
+ *
+ * Expert e lives on destination e / (E / R). With a = t * k + j:
+ *   expert_demand[e]  = #{a : topk_idx[a] == e}
+ *   rank(a)           = #{a' < a : topk_idx[a'] == topk_idx[a]}
+ *   kept(a)           = capacity < 0 || rank(a) < capacity
+ *   expert_counts[e]  = kept replicas of e = min(demand, capacity)
+ *   expert_offsets    = exclusive prefix sum of counts, E + 1 entries;
+ *                       expert_offsets[E] = N, the kept total
+ *   dest_counts[r]    = sum of counts of r's experts
+ *   dest_offsets[r]   = expert_offsets[r * E / R]; dest_offsets[R] = N
+ *   pos[a]            = expert_offsets[e] + rank(a) if kept, else -1
+ *   send_src[pos[a]]  = t for every kept a (send_src may be NULL)
+ * The send rows are thereby grouped by destination, then by expert, then
+ * by token. N stays on the device (expert_offsets[E]).
+ *
+ * Arguments:
+ *   topk_idx  [T][k] int32 expert ids. Precondition: every id in [0, E)
+ *             and distinct within a row; ids outside [0, E) are ignored
+ *             (not counted, pos = -1).
+ *   capacity  < 0: dropless; >= 0: at most `capacity` rows per expert.
+ *   outputs   int32 arrays of the sizes above; send_src, when given,
+ *             holds at least N entries: T * k when dropless, else
+ *             min(T * k, E * capacity) (entries >= N are not written).
+ *   workspace device memory of at least moe_layout_workspace_size() bytes,
+ *             16-byte aligned; its contents on entry do not matter.
+ * Errors: MOE_ERR_INVALID_ARG for NULL/misaligned pointers, T < 0, R < 1 or
+ *   E % R != 0; MOE_ERR_UNSUPPORTED outside the limits; MOE_ERR_WORKSPACE
+ *   when the workspace is NULL or too small.
+ */
+moe_status_t moe_dispatch_layout(const int32_t *topk_idx, int64_t T,
+                                 int32_t E, int32_t k, int32_t R,
+                                 int32_t capacity, int32_t *expert_demand,
+                                 int32_t *expert_counts,
+                                 int32_t *expert_offsets, int32_t *dest_counts,
+                                 int32_t *dest_offsets, int32_t *pos,
+                                 int32_t *send_src, void *workspace,
+                                 size_t workspace_bytes, void *stream);
+
+/*
+ * moe_dispatch_permute -- pack each kept replica of each token into its
+ * send row: send[pos[t][j]][:] = x[t][:] (a bit copy of the bf16 row).
+ *
+ * Defined by: aicassindra "gpu_moe_all_to_all", "Bucketing" (permute so that
+ * everything bound for one destination is contiguous, fused into the
+ * staging kernel) and "Two collectives per layer" (each token goes out k
+ * times); thecoregrid "Mixture-of-experts acceleration through overlap",
+ * paragraph on the remote-owner-aligned layout (each block of rows belongs
+ * to one destination, so it leaves as one contiguous write).
+ *
+ * Arguments:
+ *   x         [T][H] bf16, 16-byte aligned.
+ *   pos       [T][k] int32 from moe_dispatch_layout (-1 = dropped).
+ *   send      [send_rows][H] bf16 out, 16-byte aligned. Rows that no
+ *             replica points at are not written. send_rows must cover N
+ *             (T * k when dropless, min(T * k, E * capacity) otherwise);
+ *             positions >= send_rows are skipped (a broken precondition,
+ *             never a write out of bounds).
+ * Errors: MOE_ERR_INVALID_ARG for NULL/misaligned pointers, T < 0,
+ *   send_rows < 0; MOE_ERR_UNSUPPORTED outside the limits.
+ */
+moe_status_t moe_dispatch_permute(const uint16_t *x, const int32_t *pos,
+                                  int64_t T, int32_t H, int32_t k,
+                                  uint16_t *send, int64_t send_rows,
+                                  void *stream);
+
+/*
+ * moe_combine_reduce -- bring each token's k expert outputs back along the
+ * inverse permutation and reduce them at the origin:
+ *   out[t][h] = round( sum_{j : pos[t][j] >= 0} topk_w[t][j] * y[pos[t][j]][h]
+ *                      + shared[t][h] + residual[t][h] )
+ * accumulated in float32 with one fused multiply-add per kept replica in
+ * ascending j, then + shared, then + residual, and one final rounding to
+ * bf16 (nearest, ties to even) unless MOE_COMBINE_OUT_FP32 is set. Dropped
+ * replicas contribute nothing; the other weights are not renormalised.
+ *
+ * Defined by: aicassindra "gpu_moe_all_to_all", "Two collectives per layer"
+ * (outputs return along the inverse permutation, k partial results per
+ * token, scaled by the gate weights at the origin); "MoE All-to-All
+ * Dispatch and Ragged Routing", "Returning Tokens to the Original GPU" (the
+ * residual x + dx is formed at the origin); ai-from-scratch "19.
+ * All-to-all", section on 512 experts (10 routed + 1 always-active shared
+ * expert) and "Why the router can ruin your day" (drops).
+ *
+ * Arguments:
+ *   y         [y_rows][H] bf16 expert outputs in send layout, 16-byte
+ *             aligned (may alias the send buffer of moe_dispatch_permute).
+ *   pos       [T][k] int32; positions >= y_rows are skipped (a broken
+ *             precondition, never a read out of bounds).
+ *   topk_w    [T][k] float32.
+ *   shared    [T][H] bf16 shared-expert output or NULL (weight 1).
+ *   residual  [T][H] bf16 or NULL.
+ *   out       [T][H] bf16, or float32 with MOE_COMBINE_OUT_FP32; 16-byte
+ *             aligned; must not alias any input.
+ * Errors: MOE_ERR_INVALID_ARG for NULL/misaligned pointers, T < 0,
+ *   y_rows < 0; MOE_ERR_UNSUPPORTED outside the limits.
+ */
+moe_status_t moe_combine_reduce(const uint16_t *y, int64_t y_rows,
+                                const int32_t *pos, const float *topk_w,
+                                const uint16_t *shared,
+                                const uint16_t *residual, int64_t T,
+                                int32_t H, int32_t k, uint32_t flags,
+                                void *out, void *stream);
+
+/* moe_status_string -- a static, human-readable name for a status. */
+const char *moe_status_string(moe_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EP_H */

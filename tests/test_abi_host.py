@@ -1,0 +1,114 @@
+"""The C ABI library loads, exports what include/moe_ep.h declares, and
+rejects bad arguments on the host, before anything touches a GPU.
+
+Only argument-validation paths are called here (no GPU in this container):
+each call below fails a check that comes before any HIP call, so the
+pointers passed are never dereferenced.
+"""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ep.h")
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import combine_route_topk_amd
+    return combine_route_topk_amd
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(moe):
+    declared = _declared_functions()
+    assert declared == sorted(moe.EXPORTS)
+    raw = ctypes.CDLL(moe.LIB_PATH)
+    for name in declared:
+        assert hasattr(raw, name), name
+
+
+def test_status_strings(moe):
+    for code in range(5):
+        assert moe.moe_status_string(code).startswith("MOE_")
+    assert "unknown" in moe.moe_status_string(99)
+
+
+FAKE = 0x10000          # never dereferenced: every call below fails validation first
+MIS = 0x10002           # misaligned for 4- and 16-byte requirements
+
+
+def test_route_validation(moe):
+    lib = moe.lib
+    assert lib.moe_route_topk(FAKE, None, -1, 8, 2, 1, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_topk(FAKE, None, 4, 8, 0, 1, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_topk(FAKE, None, 4, 8, 9, 1, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_topk(FAKE, None, 4, 2048, 2, 1, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_topk(FAKE, None, 4, 64, 33, 1, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_topk(FAKE, None, 2 ** 29, 64, 4, 1, FAKE, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_route_topk(FAKE, None, 4, 8, 2, 6, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_topk(None, None, 4, 8, 2, 1, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_topk(MIS, None, 4, 8, 2, 1, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_topk(FAKE, MIS, 4, 8, 2, 1, FAKE, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    # T = 0 is a no-op that needs no pointers and enqueues nothing
+    assert lib.moe_route_topk(None, None, 0, 8, 2, 1, None, None, None) == moe.MOE_OK
+
+
+def test_workspace_size(moe):
+    # one E-wide int32 histogram per tile of 2048 assignments
+    assert moe.moe_layout_workspace_size(32768, 512, 10, 64) == 160 * 512 * 4
+    assert moe.moe_layout_workspace_size(256, 16, 2, 4) == 1 * 16 * 4
+    assert moe.moe_layout_workspace_size(0, 16, 2, 4) == 0
+    with pytest.raises(moe.MoeError):
+        moe.moe_layout_workspace_size(256, 16, 2, 3)      # E % R != 0
+    with pytest.raises(moe.MoeError):
+        moe.moe_layout_workspace_size(256, 16, 17, 4)     # k > E
+
+
+def _layout(lib, T=256, E=16, k=2, R=4, cap=-1, idx=FAKE, pos=FAKE, ws=FAKE, ws_bytes=1 << 20, out=FAKE):
+    return lib.moe_dispatch_layout(idx, T, E, k, R, cap, out, out, out, out, out, pos, None,
+                                   ws, ws_bytes, None)
+
+
+def test_layout_validation(moe):
+    lib = moe.lib
+    assert _layout(lib, R=3) == moe.MOE_ERR_INVALID_ARG
+    assert _layout(lib, R=0) == moe.MOE_ERR_INVALID_ARG
+    assert _layout(lib, T=-1) == moe.MOE_ERR_INVALID_ARG
+    assert _layout(lib, E=2000, R=1) == moe.MOE_ERR_UNSUPPORTED
+    assert _layout(lib, k=40) == moe.MOE_ERR_UNSUPPORTED
+    assert _layout(lib, idx=None) == moe.MOE_ERR_INVALID_ARG
+    assert _layout(lib, pos=MIS) == moe.MOE_ERR_INVALID_ARG
+    assert _layout(lib, out=None) == moe.MOE_ERR_INVALID_ARG
+    assert _layout(lib, ws=None) == moe.MOE_ERR_WORKSPACE
+    assert _layout(lib, ws_bytes=63) == moe.MOE_ERR_WORKSPACE
+    assert _layout(lib, ws=FAKE + 8) == moe.MOE_ERR_WORKSPACE
+
+
+def test_permute_and_combine_validation(moe):
+    lib = moe.lib
+    assert lib.moe_dispatch_permute(FAKE, FAKE, 4, 12, 2, FAKE, 8, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_dispatch_permute(FAKE, FAKE, 4, 16, 2, FAKE, -1, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch_permute(FAKE + 4, FAKE, 4, 16, 2, FAKE, 8, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch_permute(None, FAKE, 4, 16, 2, FAKE, 8, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_dispatch_permute(None, None, 0, 16, 2, None, 0, None) == moe.MOE_OK
+    assert lib.moe_combine_reduce(FAKE, 8, FAKE, FAKE, None, None, 4, 16, 2, 2, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine_reduce(FAKE, 8, FAKE, FAKE, None, None, 4, 0, 2, 0, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_combine_reduce(FAKE, 8, FAKE, FAKE, MIS, None, 4, 16, 2, 0, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine_reduce(FAKE, 8, FAKE, FAKE, None, None, 4, 16, 2, 0, None, None) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_combine_reduce(None, 0, None, None, None, None, 0, 16, 2, 0, None, None) == moe.MOE_OK
+
+
+def test_binding_refuses_host_tensors(moe):
+    import torch
+    with pytest.raises(ValueError):
+        moe.moe_route_topk(torch.zeros(4, 8), None, 2, topk_idx=torch.zeros(4, 2, dtype=torch.int32),
+                           topk_w=torch.zeros(4, 2), stream=0)

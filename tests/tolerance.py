@@ -30,4 +30,6 @@ def assert_bf16_close(got_bits, ref_bits, atol, ulps=1, err_msg=""):
             f"{err_msg}: {bad.sum()} of {bad.size} bf16 values off by more than {ulps} ulp "
             f"and {atol} abs; first at flat {i.tolist()}: got {bf16_value(got_bits.ravel()[i]).tolist()} "
             f"ref {bf16_value(ref_bits.ravel()[i]).tolist()}")
-    return int(d_ulp.max()) if d_ulp.size else 0
+    # report the largest step difference away from zero and how many differ
+    away = np.abs(bf16_value(ref_bits)) > 1e-3
+    return (int(d_ulp[away].max()) if away.any() else 0), int((d_ulp > 0).sum())
