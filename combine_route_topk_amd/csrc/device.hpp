@@ -73,6 +73,94 @@ __device__ __forceinline__ int32_t wave_inclusive_sum(int32_t v)
     return v;
 }
 
+// Row-level all-reductions with DPP lane permutations. After the four
+// steps every lane of a 16-lane row holds the row's result; every step
+// combines two groups whose lanes already agree (pairs, quads, 8-lane
+// halves), so the result is the same on every lane of the row and does not
+// depend on which lane computes it. The four row results are combined on
+// the scalar unit by the callers below.
+namespace dpp {
+constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kRowHalfMirror = 0x141;  // lane i of 8 <- lane 7 - i
+constexpr int kRowMirror = 0x140;      // lane i of 16 <- lane 15 - i
+
+template <int CTRL>
+__device__ __forceinline__ uint32_t mov(uint32_t v)
+{
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+}  // namespace dpp
+
+__device__ __forceinline__ uint32_t row_max_u32(uint32_t v)
+{
+    v = max(v, dpp::mov<dpp::kQuadSwap1>(v));
+    v = max(v, dpp::mov<dpp::kQuadSwap2>(v));
+    v = max(v, dpp::mov<dpp::kRowHalfMirror>(v));
+    return max(v, dpp::mov<dpp::kRowMirror>(v));
+}
+
+__device__ __forceinline__ uint32_t row_min_u32(uint32_t v)
+{
+    v = min(v, dpp::mov<dpp::kQuadSwap1>(v));
+    v = min(v, dpp::mov<dpp::kQuadSwap2>(v));
+    v = min(v, dpp::mov<dpp::kRowHalfMirror>(v));
+    return min(v, dpp::mov<dpp::kRowMirror>(v));
+}
+
+__device__ __forceinline__ float row_sum_f32(float v)
+{
+    v += __uint_as_float(dpp::mov<dpp::kQuadSwap1>(__float_as_uint(v)));
+    v += __uint_as_float(dpp::mov<dpp::kQuadSwap2>(__float_as_uint(v)));
+    v += __uint_as_float(dpp::mov<dpp::kRowHalfMirror>(__float_as_uint(v)));
+    return v + __uint_as_float(dpp::mov<dpp::kRowMirror>(__float_as_uint(v)));
+}
+
+__device__ __forceinline__ float row_max_f32(float v)
+{
+    v = fmaxf(v, __uint_as_float(dpp::mov<dpp::kQuadSwap1>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp::mov<dpp::kQuadSwap2>(__float_as_uint(v))));
+    v = fmaxf(v, __uint_as_float(dpp::mov<dpp::kRowHalfMirror>(__float_as_uint(v))));
+    return fmaxf(v, __uint_as_float(dpp::mov<dpp::kRowMirror>(__float_as_uint(v))));
+}
+
+__device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane)
+{
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+
+// Wave-wide results, uniform (held in scalar registers).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
+{
+    v = row_max_u32(v);
+    return max(max(readlane_u32(v, 0), readlane_u32(v, 16)),
+               max(readlane_u32(v, 32), readlane_u32(v, 48)));
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
+{
+    v = row_min_u32(v);
+    return min(min(readlane_u32(v, 0), readlane_u32(v, 16)),
+               min(readlane_u32(v, 32), readlane_u32(v, 48)));
+}
+
+// Fixed association order: (row0 + row1) + (row2 + row3).
+__device__ __forceinline__ float wave_sum_f32_dpp(float v)
+{
+    v = row_sum_f32(v);
+    const uint32_t u = __float_as_uint(v);
+    return (__uint_as_float(readlane_u32(u, 0)) + __uint_as_float(readlane_u32(u, 16))) +
+           (__uint_as_float(readlane_u32(u, 32)) + __uint_as_float(readlane_u32(u, 48)));
+}
+
+__device__ __forceinline__ float wave_max_f32_dpp(float v)
+{
+    v = row_max_f32(v);
+    const uint32_t u = __float_as_uint(v);
+    return fmaxf(fmaxf(__uint_as_float(readlane_u32(u, 0)), __uint_as_float(readlane_u32(u, 16))),
+                 fmaxf(__uint_as_float(readlane_u32(u, 32)), __uint_as_float(readlane_u32(u, 48))));
+}
+
 // bf16 <-> float. A bf16 value is the top half of a float32 pattern, so
 // widening is a shift; narrowing uses gfx950's packed convert, which rounds
 // to nearest, ties to even, and quiets NaNs.

@@ -10,8 +10,10 @@
 // 16 bytes per lane, and writes it to each of the token's kept send rows.
 // Row reads and writes are contiguous 16-byte-per-lane streams, so a wave
 // moves 1 KiB per instruction. Tokens whose replicas were all dropped
-// skip the read. Both streams carry the non-temporal hint: x is read once
-// and send is not read again by this kernel.
+// skip the read. The send rows are written with the non-temporal hint
+// (streamed out, not kept in cache); x is read with an ordinary load. On
+// MI355X that pairing measured fastest: 5.7 TB/s for k = 10 against 4.8 TB/s
+// with the hint on both streams.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -34,7 +36,7 @@ __global__ __launch_bounds__(kRowThreads) void permute_kernel(
     }
     if (!any || c >= C16)
         return;
-    const u32x4 v = load_stream(x + t * C16 + c);
+    const u32x4 v = x[t * C16 + c];
     for (int j = 0; j < k; ++j) {
         const int32_t p = pr[j];
         if (p >= 0 && p < send_rows)

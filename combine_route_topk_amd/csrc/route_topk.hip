@@ -9,12 +9,15 @@
 //
 // Layout on gfx950: lane l of the wave owns experts l, l + 64, l + 128, ...
 // (KPL = ceil(E / 64) registers), so each load instruction reads 256
-// contiguous bytes of the logit row. Each selection round takes a wave-wide
-// maximum of one 64-bit key per lane -- the lane's best score key in the
-// high half and the inverted expert id in the low half, which breaks ties
-// towards the smaller id -- then only the owning lane drops the winner and
-// refreshes its best. The k results land on lanes 0..k-1, which compute the
-// softmax and write one coalesced row of ids and weights.
+// contiguous bytes of the logit row. Scores become order-preserving 32-bit
+// keys. Each lane keeps its two best remaining (key, id, logit) candidates;
+// a selection round is a wave-wide 32-bit maximum (DPP within rows, then
+// four readlanes on the scalar unit), a ballot of the lanes holding that
+// key, and -- only when two lanes tie on the key -- a wave minimum of their
+// expert ids, so ties go to the smaller id. The winning lane pops its
+// candidate and rescans its registers only when both candidates are used
+// up. Round j's id and logit are kept by lane j, so lanes
+// 0..k-1 finish with the softmax and one coalesced row of ids and weights.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -25,42 +28,26 @@ constexpr int kRouteThreads = 256;
 constexpr int kTokensPerBlock = kRouteThreads / kWave;
 
 // Order-preserving map of a float score onto uint32: larger key = higher
-// rank. -0 and +0 share a key; every NaN maps to 1, below -inf
-// (0x007FFFFF); 0 is left for padding lanes and removed entries.
+// rank. The caller adds +0.0f first, which turns -0 into +0 and leaves
+// every other value unchanged, so equal reals get equal keys. Every NaN
+// maps to 1, below -inf (0x007FFFFF); 0 marks padding and used entries.
 __device__ __forceinline__ uint32_t score_key(float s)
 {
-    if (s != s)
-        return 1u;
-    uint32_t u = __float_as_uint(s);
-    if ((u << 1) == 0u)
-        u = 0u;
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t u = __float_as_uint(s);
+    const uint32_t k = u ^ (uint32_t)(((int32_t)u >> 31) | (int32_t)0x80000000);
+    return s != s ? 1u : k;
 }
 
-template <int KPL>
-struct LaneExperts {
-    uint32_t key[KPL];
-    float logit[KPL];
-    // best entry of this lane: key, expert id, unbiased logit
-    uint32_t bk, be;
-    float bl;
-
-    __device__ __forceinline__ void refresh_best(int lane)
-    {
-        bk = 0u;
-        be = 0xFFFFFFFFu;
-        bl = 0.f;
-#pragma unroll
-        for (int i = 0; i < KPL; ++i) {
-            // ascending i is ascending expert id, so ">" keeps the lower id on ties
-            if (key[i] > bk) {
-                bk = key[i];
-                be = (uint32_t)(i * kWave + lane);
-                bl = logit[i];
-            }
-        }
-    }
+struct Candidate {
+    uint32_t key, id;
+    float logit;
 };
+
+__device__ __forceinline__ bool ranks_below(uint32_t key, uint32_t id, uint32_t ref_key,
+                                            uint32_t ref_id)
+{
+    return key < ref_key || (key == ref_key && id > ref_id);
+}
 
 template <int KPL>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
@@ -73,67 +60,99 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
         return;  // t is uniform across the wave: whole waves leave together
     const float *row = logits + t * E;
 
-    LaneExperts<KPL> le;
+    uint32_t key[KPL];
+    float logit[KPL];
 #pragma unroll
     for (int i = 0; i < KPL; ++i) {
         const int e = i * kWave + lane;
         if (e < E) {
             const float v = row[e];
-            le.logit[i] = v;
-            le.key[i] = score_key(bias ? v + bias[e] : v);
+            logit[i] = v;
+            key[i] = score_key((bias ? v + bias[e] : v) + 0.0f);
         } else {
-            le.logit[i] = 0.f;
-            le.key[i] = 0u;  // padding ranks below everything, NaN included
+            logit[i] = 0.f;
+            key[i] = 0u;
         }
     }
-    le.refresh_best(lane);
 
-    int32_t my_e = 0;
+    // the lane's two best entries; ascending i is ascending id, so strict
+    // comparisons keep the smaller id first among equal keys
+    Candidate c1 = {0u, 0xFFFFFFFFu, 0.f}, c2 = {0u, 0xFFFFFFFFu, 0.f};
+#pragma unroll
+    for (int i = 0; i < KPL; ++i) {
+        const Candidate c = {key[i], (uint32_t)(i * kWave + lane), logit[i]};
+        if (c.key > c1.key) {
+            c2 = c1;
+            c1 = c;
+        } else if (c.key > c2.key) {
+            c2 = c;
+        }
+    }
+
+    uint32_t my_e = 0;
     float my_l = 0.f;
     float m = -INFINITY;  // max unbiased logit among the selected
     for (int j = 0; j < k; ++j) {
-        const uint64_t key = ((uint64_t)le.bk << 32) | (uint32_t)~le.be;
-        const uint64_t best = wave_max_u64(key);
-        const uint32_t ew = (uint32_t)__builtin_amdgcn_readfirstlane((int)~(uint32_t)best);
-        const int owner = (int)(ew & (kWave - 1));
-        const int slot = (int)(ew / kWave);
-        const float lw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(le.bl), owner));
+        const uint32_t best = wave_max_u32(c1.key);
+        const uint64_t holders = ballot64(c1.key == best);
+        int owner;
+        uint32_t ew;
+        if (__popcll(holders) == 1) {
+            owner = __ffsll((unsigned long long)holders) - 1;
+            ew = readlane_u32(c1.id, owner);
+        } else {  // several lanes hold an equal key: the smallest id wins
+            ew = wave_min_u32(c1.key == best ? c1.id : 0xFFFFFFFFu);
+            owner = (int)(ew & (kWave - 1));
+        }
+        const float lw = __uint_as_float(readlane_u32(__float_as_uint(c1.logit), owner));
         if (lane == j) {
-            my_e = (int32_t)ew;
+            my_e = ew;
             my_l = lw;
         }
         m = fmaxf(m, lw);
         if (lane == owner) {
+            const uint32_t gone_key = c1.key, gone_id = c1.id;
+            c1 = c2;
+            c2 = {0u, 0xFFFFFFFFu, 0.f};
+            if (c1.key == 0u) {
+                // both candidates used: rescan the entries ranked below the
+                // last one taken from this lane
 #pragma unroll
-            for (int i = 0; i < KPL; ++i)
-                if (i == slot)
-                    le.key[i] = 0u;
-            le.refresh_best(lane);
+                for (int i = 0; i < KPL; ++i) {
+                    const Candidate c = {key[i], (uint32_t)(i * kWave + lane), logit[i]};
+                    if (!ranks_below(c.key, c.id, gone_key, gone_id))
+                        continue;
+                    if (c.key > c1.key) {
+                        c2 = c1;
+                        c1 = c;
+                    } else if (c.key > c2.key) {
+                        c2 = c;
+                    }
+                }
+            }
         }
     }
 
     float w;
     if (normalize) {
         const float u = lane < k ? expf(my_l - m) : 0.f;
-        const float s = wave_sum_f32(u);
-        w = u / s;
+        w = u / wave_sum_f32_dpp(u);
     } else {
         float lm = -INFINITY;
 #pragma unroll
         for (int i = 0; i < KPL; ++i)
             if (i * kWave + lane < E)
-                lm = fmaxf(lm, le.logit[i]);
-        const float M = wave_max_f32(lm);
+                lm = fmaxf(lm, logit[i]);
+        const float M = wave_max_f32_dpp(lm);
         float part = 0.f;
 #pragma unroll
         for (int i = 0; i < KPL; ++i)
             if (i * kWave + lane < E)
-                part += expf(le.logit[i] - M);
-        const float s = wave_sum_f32(part);
-        w = (lane < k ? expf(my_l - M) : 0.f) / s;
+                part += expf(logit[i] - M);
+        w = (lane < k ? expf(my_l - M) : 0.f) / wave_sum_f32_dpp(part);
     }
     if (lane < k) {
-        topk_idx[t * k + lane] = my_e;
+        topk_idx[t * k + lane] = (int32_t)my_e;
         topk_w[t * k + lane] = w;
     }
 }
