@@ -73,92 +73,70 @@ __device__ __forceinline__ int32_t wave_inclusive_sum(int32_t v)
     return v;
 }
 
-// Row-level all-reductions with DPP lane permutations. After the four
-// steps every lane of a 16-lane row holds the row's result; every step
-// combines two groups whose lanes already agree (pairs, quads, 8-lane
-// halves), so the result is the same on every lane of the row and does not
-// depend on which lane computes it. The four row results are combined on
-// the scalar unit by the callers below.
+// Wave-wide reductions with DPP lane permutations, for commutative and
+// associative operations with an identity. Four steps combine pairs,
+// quads, 8-lane halves and 16-lane rows (after each step the lanes of a
+// group agree); row_bcast:15 then folds row 0 into row 1 and row 2 into row
+// 3, and row_bcast:31 folds rows 0-1 into rows 2-3, so lane 63 ends with
+// the result of the whole wave. The association order is fixed, so float
+// results are reproducible. The result is read back as a uniform value.
 namespace dpp {
-constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]: lane ^ 1
-constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]: lane ^ 2
+constexpr int kQuadSwap1 = 0xB1;       // quad_perm [1,0,3,2]: lane ^ 1
+constexpr int kQuadSwap2 = 0x4E;       // quad_perm [2,3,0,1]: lane ^ 2
 constexpr int kRowHalfMirror = 0x141;  // lane i of 8 <- lane 7 - i
 constexpr int kRowMirror = 0x140;      // lane i of 16 <- lane 15 - i
+constexpr int kRowBcast15 = 0x142;     // row r <- lane 15 of row r - 1
+constexpr int kRowBcast31 = 0x143;     // rows 2, 3 <- lane 31
 
-template <int CTRL>
-__device__ __forceinline__ uint32_t mov(uint32_t v)
+// lanes of rows outside row_mask read `identity`
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ uint32_t mov(uint32_t v, uint32_t identity)
 {
-    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+    return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, ROW_MASK, 0xF, false);
 }
 }  // namespace dpp
 
-__device__ __forceinline__ uint32_t row_max_u32(uint32_t v)
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_bits(uint32_t v, uint32_t identity, Op op)
 {
-    v = max(v, dpp::mov<dpp::kQuadSwap1>(v));
-    v = max(v, dpp::mov<dpp::kQuadSwap2>(v));
-    v = max(v, dpp::mov<dpp::kRowHalfMirror>(v));
-    return max(v, dpp::mov<dpp::kRowMirror>(v));
+    v = op(v, dpp::mov<dpp::kQuadSwap1>(v, identity));
+    v = op(v, dpp::mov<dpp::kQuadSwap2>(v, identity));
+    v = op(v, dpp::mov<dpp::kRowHalfMirror>(v, identity));
+    v = op(v, dpp::mov<dpp::kRowMirror>(v, identity));
+    v = op(v, dpp::mov<dpp::kRowBcast15, 0xA>(v, identity));
+    v = op(v, dpp::mov<dpp::kRowBcast31, 0xC>(v, identity));
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
 
-__device__ __forceinline__ uint32_t row_min_u32(uint32_t v)
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
 {
-    v = min(v, dpp::mov<dpp::kQuadSwap1>(v));
-    v = min(v, dpp::mov<dpp::kQuadSwap2>(v));
-    v = min(v, dpp::mov<dpp::kRowHalfMirror>(v));
-    return min(v, dpp::mov<dpp::kRowMirror>(v));
+    return wave_reduce_bits(v, 0u, [](uint32_t a, uint32_t b) { return max(a, b); });
 }
 
-__device__ __forceinline__ float row_sum_f32(float v)
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
 {
-    v += __uint_as_float(dpp::mov<dpp::kQuadSwap1>(__float_as_uint(v)));
-    v += __uint_as_float(dpp::mov<dpp::kQuadSwap2>(__float_as_uint(v)));
-    v += __uint_as_float(dpp::mov<dpp::kRowHalfMirror>(__float_as_uint(v)));
-    return v + __uint_as_float(dpp::mov<dpp::kRowMirror>(__float_as_uint(v)));
+    return wave_reduce_bits(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return min(a, b); });
 }
 
-__device__ __forceinline__ float row_max_f32(float v)
+__device__ __forceinline__ float wave_max_f32_dpp(float v)
 {
-    v = fmaxf(v, __uint_as_float(dpp::mov<dpp::kQuadSwap1>(__float_as_uint(v))));
-    v = fmaxf(v, __uint_as_float(dpp::mov<dpp::kQuadSwap2>(__float_as_uint(v))));
-    v = fmaxf(v, __uint_as_float(dpp::mov<dpp::kRowHalfMirror>(__float_as_uint(v))));
-    return fmaxf(v, __uint_as_float(dpp::mov<dpp::kRowMirror>(__float_as_uint(v))));
+    return __uint_as_float(wave_reduce_bits(__float_as_uint(v), __float_as_uint(-INFINITY),
+                                            [](uint32_t a, uint32_t b) {
+                                                return __float_as_uint(
+                                                    fmaxf(__uint_as_float(a), __uint_as_float(b)));
+                                            }));
+}
+
+__device__ __forceinline__ float wave_sum_f32_dpp(float v)
+{
+    return __uint_as_float(wave_reduce_bits(__float_as_uint(v), 0u, [](uint32_t a, uint32_t b) {
+        return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+    }));
 }
 
 __device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane)
 {
     return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
-}
-
-// Wave-wide results, uniform (held in scalar registers).
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
-{
-    v = row_max_u32(v);
-    return max(max(readlane_u32(v, 0), readlane_u32(v, 16)),
-               max(readlane_u32(v, 32), readlane_u32(v, 48)));
-}
-
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
-{
-    v = row_min_u32(v);
-    return min(min(readlane_u32(v, 0), readlane_u32(v, 16)),
-               min(readlane_u32(v, 32), readlane_u32(v, 48)));
-}
-
-// Fixed association order: (row0 + row1) + (row2 + row3).
-__device__ __forceinline__ float wave_sum_f32_dpp(float v)
-{
-    v = row_sum_f32(v);
-    const uint32_t u = __float_as_uint(v);
-    return (__uint_as_float(readlane_u32(u, 0)) + __uint_as_float(readlane_u32(u, 16))) +
-           (__uint_as_float(readlane_u32(u, 32)) + __uint_as_float(readlane_u32(u, 48)));
-}
-
-__device__ __forceinline__ float wave_max_f32_dpp(float v)
-{
-    v = row_max_f32(v);
-    const uint32_t u = __float_as_uint(v);
-    return fmaxf(fmaxf(__uint_as_float(readlane_u32(u, 0)), __uint_as_float(readlane_u32(u, 16))),
-                 fmaxf(__uint_as_float(readlane_u32(u, 32)), __uint_as_float(readlane_u32(u, 48))));
 }
 
 // bf16 <-> float. A bf16 value is the top half of a float32 pattern, so

@@ -13,16 +13,27 @@ hipError_t launch_route_topk(const float *logits, const float *bias, int64_t T, 
                              int32_t k, bool normalize, int32_t *topk_idx, float *topk_w,
                              hipStream_t stream);
 
-// Assignments (t, j) are handled in tiles of kLayoutTile; the workspace holds
-// one E-wide histogram per tile.
+// Layout plan. Up to kSmallAssignments assignments (and E <= 512) one block
+// does the whole layout. Above that, assignments are split into at most
+// kMaxTiles tiles of at least kLayoutTile; the workspace holds one E-wide
+// int32 histogram per tile.
 constexpr int kLayoutThreads = 256;
-constexpr int kLayoutPerThread = 8;
-constexpr int kLayoutTile = kLayoutThreads * kLayoutPerThread;
+constexpr int64_t kLayoutTile = 2048;
+constexpr int64_t kMaxTiles = 128;
+constexpr int64_t kSmallAssignments = 4096;
+constexpr int32_t kSmallMaxExperts = 512;
 
-inline int64_t layout_tiles(int64_t TK) { return (TK + kLayoutTile - 1) / kLayoutTile; }
+struct LayoutPlan {
+    bool small;
+    int64_t tile;   // assignments per tile (large path)
+    int64_t tiles;  // number of tiles (large path), 0 otherwise
+};
+
+LayoutPlan layout_plan(int64_t TK, int32_t E);
+
 inline size_t layout_workspace_bytes(int64_t TK, int32_t E)
 {
-    return (size_t)layout_tiles(TK) * (size_t)E * sizeof(int32_t);
+    return (size_t)layout_plan(TK, E).tiles * (size_t)E * sizeof(int32_t);
 }
 
 hipError_t launch_dispatch_layout(const int32_t *topk_idx, int64_t T, int32_t E, int32_t k,

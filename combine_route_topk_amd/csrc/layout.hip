@@ -11,189 +11,310 @@
 // The layout is a stable counting sort of the T*k assignments by expert id
 // (experts sit on destinations in contiguous blocks, so this also groups by
 // destination). Positions must be bit-exact, so every rank is derived in
-// token order, never from the order in which atomics happen to land:
+// assignment order, never from the order in which atomics happen to land;
+// LDS atomics only build counts, whose totals do not depend on order.
 //
-//   1. layout_count_kernel: one block per tile of kLayoutTile assignments
-//      builds an E-bin LDS histogram (integer atomics: the totals do not
-//      depend on their order) and writes it to the workspace.
-//   2. layout_scan_kernel: one block per 64 experts turns the per-tile
-//      histograms into exclusive prefixes over tiles (in place) and writes
-//      demand and kept counts.
-//   3. layout_rank_kernel: each block rebuilds the expert offsets with an
-//      LDS scan over E (block 0 publishes them with the destination counts),
-//      then ranks its tile. Each wave owns 512 consecutive assignments and
-//      walks them 64 at a time; lanes holding the same expert find each
-//      other with a bit-sliced match (one ballot per bit of the id), so the
-//      rank inside a step is a popcount of the lanes below, and the lowest
-//      such lane bumps the wave's LDS counter. A per-expert prefix over the
-//      4 waves plus the tile's prefix from step 2 gives the global rank.
+// The work is tiny in bytes and latency-bound (the pages make the same point
+// about the counts exchange), so the design minimises kernel launches and
+// block-wide round trips:
+//  * T*k <= kSmallAssignments and E <= 512: one 1024-thread block does
+//    everything. Each of its 16 waves owns a contiguous range of assignments and counts it
+//    into its own LDS row (pass A); a prefix over the waves gives each
+//    wave's first rank per expert, a block scan gives the offsets; then each
+//    wave walks its range again in order (pass B), 64 assignments at a time:
+//    lanes holding the same expert find each other with a bit-sliced match
+//    (one ballot per bit of the id), the rank is the wave's running count
+//    plus the popcount of matching lower lanes, and the lowest matching lane
+//    advances the count.
+//  * larger: layout_count_kernel writes one E-bin histogram per tile (at
+//    most kMaxTiles tiles); layout_rank_kernel then gives every tile one
+//    block that reads all the histograms from L2 (spread over its threads,
+//    summed with LDS integer atomics), derives the totals, its tile's prefix
+//    and the offsets itself, and ranks its tile with the same two passes
+//    over 16 waves (8 when E > 512). Block 0 publishes counts and offsets.
 #include "device.hpp"
 #include "launch.hpp"
 
 namespace moe {
 namespace {
 
-constexpr int kScanWaves = 16;
-constexpr int kRankWaves = kLayoutThreads / kWave;
-constexpr int kWaveSpan = kLayoutTile / kRankWaves;
-constexpr int kSteps = kWaveSpan / kWave;
+constexpr int kSmallThreads = 1024;
+constexpr int kSmallWaves = kSmallThreads / kWave;
+
+// Assignments are read kBatch steps of 64 at a time, so that each wave has
+// kBatch independent loads in flight instead of one load per step.
+constexpr int kBatch = 8;
+
+// Rank the assignments [a_begin, a_end) of one wave in order. `run` is the
+// wave's LDS row: on entry its first rank per expert, on exit advanced past
+// the range. Writes pos and send_src.
+__device__ __forceinline__ void rank_range(const int32_t *__restrict__ idx, int64_t a_begin,
+                                           int64_t a_end, int32_t k, int32_t E, int32_t capacity,
+                                           int nbits, int32_t *run, const int32_t *eoff,
+                                           int32_t *__restrict__ pos,
+                                           int32_t *__restrict__ send_src)
+{
+    const int lane = lane_id();
+    for (int64_t a0 = a_begin; a0 < a_end; a0 += kBatch * kWave) {
+        int32_t ev[kBatch];
+#pragma unroll
+        for (int s = 0; s < kBatch; ++s) {
+            const int64_t a = a0 + s * kWave + lane;
+            ev[s] = a < a_end ? idx[a] : -1;
+        }
+#pragma unroll
+        for (int s = 0; s < kBatch; ++s) {
+            if (a0 + s * kWave >= a_end)
+                break;  // uniform: the wave's range is exhausted
+            const int64_t a = a0 + s * kWave + lane;
+            const int32_t e = ev[s];
+            const bool valid = (uint32_t)e < (uint32_t)E;
+            uint64_t same = ballot64(valid);
+            for (int b = 0; b < nbits; ++b) {
+                const bool bit = (e >> b) & 1;
+                const uint64_t ones = ballot64(bit);
+                same &= bit ? ones : ~ones;
+            }
+            const int32_t below = (int32_t)count_below(same);
+            const int32_t seen = valid ? run[e] : 0;
+            if (valid && below == 0)
+                run[e] = seen + (int32_t)__popcll(same);
+            if (a < a_end) {
+                const int32_t r = seen + below;
+                int32_t p = -1;
+                if (valid && (capacity < 0 || r < capacity))
+                    p = eoff[e] + r;
+                pos[a] = p;
+                if (p >= 0 && send_src)
+                    send_src[p] = (int32_t)((uint32_t)a / (uint32_t)k);
+            }
+        }
+    }
+}
+
+// Exclusive scan of cnt[0..E) into eoff[0..E] with all threads of the
+// block (E <= 4 * blockDim.x). wave_total holds one int per wave.
+template <int THREADS>
+__device__ __forceinline__ void block_scan_counts(const int32_t *cnt, int32_t E, int32_t *eoff,
+                                                  int32_t *wave_total)
+{
+    constexpr int WAVES = THREADS / kWave;
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int w = tid / kWave;
+    constexpr int PER = (1024 + THREADS - 1) / THREADS;  // E <= 1024
+    int32_t c[PER];
+    int32_t mine = 0;
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int e = tid * PER + q;
+        c[q] = e < E ? cnt[e] : 0;
+        mine += c[q];
+    }
+    const int32_t inc = wave_inclusive_sum(mine);
+    if (lane == kWave - 1)
+        wave_total[w] = inc;
+    __syncthreads();
+    int32_t ex = inc - mine;
+    int32_t total = 0;
+#pragma unroll
+    for (int v = 0; v < WAVES; ++v) {
+        ex += v < w ? wave_total[v] : 0;
+        total += wave_total[v];
+    }
+#pragma unroll
+    for (int q = 0; q < PER; ++q) {
+        const int e = tid * PER + q;
+        if (e < E)
+            eoff[e] = ex;
+        ex += c[q];
+    }
+    if (tid == 0)
+        eoff[E] = total;
+}
+
+// Publish the offset table and the per-destination counts and offsets.
+__device__ __forceinline__ void publish_offsets(const int32_t *eoff, int32_t E, int32_t R,
+                                                int32_t *__restrict__ expert_offsets,
+                                                int32_t *__restrict__ dest_counts,
+                                                int32_t *__restrict__ dest_offsets)
+{
+    for (int e = threadIdx.x; e <= E; e += blockDim.x)
+        expert_offsets[e] = eoff[e];
+    const int32_t el = E / R;
+    for (int r = threadIdx.x; r < R; r += blockDim.x) {
+        dest_offsets[r] = eoff[r * el];
+        dest_counts[r] = eoff[(r + 1) * el] - eoff[r * el];
+    }
+    if (threadIdx.x == 0)
+        dest_offsets[R] = eoff[E];
+}
+
+// Count the valid ids of [a_begin, a_end) into row[] (order-free), with
+// kBatch loads in flight per lane. `first` and `stride` spread the range
+// over the lanes of one wave or over a whole block.
+__device__ __forceinline__ void count_range(const int32_t *__restrict__ idx, int64_t a_begin,
+                                            int64_t a_end, int64_t first, int64_t stride,
+                                            int32_t E, int32_t *row)
+{
+    for (int64_t a0 = a_begin + first; a0 < a_end; a0 += kBatch * stride) {
+        int32_t ev[kBatch];
+#pragma unroll
+        for (int s = 0; s < kBatch; ++s) {
+            const int64_t a = a0 + s * stride;
+            ev[s] = a < a_end ? idx[a] : -1;
+        }
+#pragma unroll
+        for (int s = 0; s < kBatch; ++s)
+            if ((uint32_t)ev[s] < (uint32_t)E)
+                atomicAdd(&row[ev[s]], 1);
+    }
+}
+
+// Range of wave w when [begin, end) is split into `parts` chunks of whole
+// 64-assignment steps.
+__device__ __forceinline__ void wave_span(int64_t begin, int64_t end, int w, int parts,
+                                          int64_t &lo, int64_t &hi)
+{
+    const int64_t steps = (end - begin + kWave - 1) / kWave;
+    const int64_t per = (steps + parts - 1) / parts;
+    lo = min(end, begin + (int64_t)w * per * kWave);
+    hi = min(end, lo + per * kWave);
+}
+
+__global__ __launch_bounds__(kSmallThreads) void layout_small_kernel(
+    const int32_t *__restrict__ idx, int64_t TK, int32_t k, int32_t E, int32_t R,
+    int32_t capacity, int nbits, int32_t *__restrict__ expert_demand,
+    int32_t *__restrict__ expert_counts, int32_t *__restrict__ expert_offsets,
+    int32_t *__restrict__ dest_counts, int32_t *__restrict__ dest_offsets,
+    int32_t *__restrict__ pos, int32_t *__restrict__ send_src)
+{
+    extern __shared__ int32_t sm[];
+    int32_t *wh = sm;                           // [kSmallWaves][E]
+    int32_t *cnt = wh + kSmallWaves * E;        // [E]
+    int32_t *eoff = cnt + E;                    // [E + 1]
+    __shared__ int32_t wave_total[kSmallWaves];
+    const int tid = threadIdx.x;
+    const int w = tid / kWave;
+
+    for (int i = tid; i < kSmallWaves * E; i += kSmallThreads)
+        wh[i] = 0;
+    __syncthreads();
+    int64_t lo, hi;
+    wave_span(0, TK, w, kSmallWaves, lo, hi);
+    count_range(idx, lo, hi, lane_id(), kWave, E, wh + w * E);  // pass A
+    __syncthreads();
+    for (int e = tid; e < E; e += kSmallThreads) {
+        int32_t run = 0;
+        for (int v = 0; v < kSmallWaves; ++v) {
+            const int32_t c = wh[v * E + e];
+            wh[v * E + e] = run;
+            run += c;
+        }
+        const int32_t kept = (capacity < 0 || run < capacity) ? run : capacity;
+        cnt[e] = kept;
+        expert_demand[e] = run;
+        expert_counts[e] = kept;
+    }
+    __syncthreads();
+    block_scan_counts<kSmallThreads>(cnt, E, eoff, wave_total);
+    __syncthreads();
+    publish_offsets(eoff, E, R, expert_offsets, dest_counts, dest_offsets);
+    rank_range(idx, lo, hi, k, E, capacity, nbits, wh + w * E, eoff, pos, send_src);  // pass B
+}
 
 __global__ __launch_bounds__(kLayoutThreads) void layout_count_kernel(
-    const int32_t *__restrict__ idx, int64_t TK, int32_t E, int32_t *__restrict__ tile_hist)
+    const int32_t *__restrict__ idx, int64_t TK, int64_t tile, int32_t E,
+    int32_t *__restrict__ tile_hist)
 {
     extern __shared__ int32_t hist[];
     for (int e = threadIdx.x; e < E; e += kLayoutThreads)
         hist[e] = 0;
     __syncthreads();
-    const int64_t base = (int64_t)blockIdx.x * kLayoutTile;
-#pragma unroll
-    for (int i = 0; i < kLayoutPerThread; ++i) {
-        const int64_t a = base + i * kLayoutThreads + threadIdx.x;
-        if (a < TK) {
-            const int32_t e = idx[a];
-            if ((uint32_t)e < (uint32_t)E)
-                atomicAdd(&hist[e], 1);
-        }
-    }
+    const int64_t begin = (int64_t)blockIdx.x * tile;
+    const int64_t end = min(TK, begin + tile);
+    count_range(idx, begin, end, threadIdx.x, kLayoutThreads, E, hist);
     __syncthreads();
     int32_t *out = tile_hist + (int64_t)blockIdx.x * E;
     for (int e = threadIdx.x; e < E; e += kLayoutThreads)
         out[e] = hist[e];
 }
 
-__global__ __launch_bounds__(kScanWaves *kWave) void layout_scan_kernel(
-    int32_t *__restrict__ tile_hist, int64_t B, int32_t E, int32_t capacity,
-    int32_t *__restrict__ demand, int32_t *__restrict__ counts)
+template <int kRankThreads>
+__global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
+    const int32_t *__restrict__ idx, int64_t TK, int64_t tile, int32_t B, int32_t k, int32_t E,
+    int32_t R, int32_t capacity, int nbits, const int32_t *__restrict__ tile_hist,
+    int32_t *__restrict__ expert_demand, int32_t *__restrict__ expert_counts,
+    int32_t *__restrict__ expert_offsets, int32_t *__restrict__ dest_counts,
+    int32_t *__restrict__ dest_offsets, int32_t *__restrict__ pos,
+    int32_t *__restrict__ send_src)
 {
-    __shared__ int32_t part[kScanWaves][kWave];
-    const int lane = threadIdx.x & (kWave - 1);
-    const int w = threadIdx.x / kWave;
-    const int32_t e = blockIdx.x * kWave + lane;
-    const bool ok = e < E;
-    // wave w owns tiles [b0, b1); the last wave's range always ends at B
-    const int64_t per = (B + kScanWaves - 1) / kScanWaves;
-    const int64_t b0 = min(B, (int64_t)w * per);
-    const int64_t b1 = min(B, b0 + per);
-    int32_t s = 0;
-    if (ok)
-        for (int64_t b = b0; b < b1; ++b)
-            s += tile_hist[b * E + e];
-    part[w][lane] = s;
-    __syncthreads();
-    int32_t run = 0;
-    for (int v = 0; v < w; ++v)
-        run += part[v][lane];
-    if (ok) {
-        for (int64_t b = b0; b < b1; ++b) {
-            const int32_t c = tile_hist[b * E + e];
-            tile_hist[b * E + e] = run;
-            run += c;
-        }
-        if (w == kScanWaves - 1) {
-            demand[e] = run;
-            counts[e] = (capacity < 0 || run < capacity) ? run : capacity;
-        }
-    }
-}
-
-__global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
-    const int32_t *__restrict__ idx, int64_t TK, int64_t B, int32_t k, int32_t E, int32_t R,
-    int32_t capacity, int nbits, const int32_t *__restrict__ tile_base,
-    const int32_t *__restrict__ counts, int32_t *__restrict__ expert_offsets,
-    int32_t *__restrict__ dest_counts, int32_t *__restrict__ dest_offsets,
-    int32_t *__restrict__ pos, int32_t *__restrict__ send_src)
-{
+    constexpr int kRankWaves = kRankThreads / kWave;
     extern __shared__ int32_t sm[];
-    int32_t *eoff = sm;            // [E + 1] expert offsets
-    int32_t *base = eoff + E + 1;  // [E] first rank of each expert in this tile
-    int32_t *wh = base + E;        // [kRankWaves][E] per-wave counts, then first ranks
+    int32_t *wh = sm;                    // [kRankWaves][E]
+    int32_t *cnt = wh + kRankWaves * E;  // [E]
+    int32_t *base = cnt + E;             // [E] first rank of each expert in this tile
+    int32_t *eoff = base + E;            // [E + 1]
     __shared__ int32_t wave_total[kRankWaves];
-
     const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
     const int w = tid / kWave;
+    const int b = blockIdx.x;
 
-    // (1) exclusive scan of the kept counts over experts, 4 experts per thread
-    int32_t c4[4];
-    int32_t mine = 0;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int e = tid * 4 + q;
-        c4[q] = e < E ? counts[e] : 0;
-        mine += c4[q];
+    // totals and this tile's prefix, straight from the tile histograms.
+    // Thread tid owns expert e = tid % E and tiles g, g + G, g + 2G, ...
+    // (g = tid / E, G = threads per expert), with 16 loads in flight; the
+    // G partial sums per expert meet in LDS through integer atomics.
+    for (int e = tid; e < E; e += kRankThreads) {
+        cnt[e] = 0;
+        base[e] = 0;
     }
-    const int32_t inc = wave_inclusive_sum(mine);
-    if (lane == kWave - 1)
-        wave_total[w] = inc;
-    for (int e = tid; e < E; e += kLayoutThreads)
-        base[e] = blockIdx.x < B ? tile_base[(int64_t)blockIdx.x * E + e] : 0;
-    for (int i = tid; i < kRankWaves * E; i += kLayoutThreads)
+    for (int i = tid; i < kRankWaves * E; i += kRankThreads)
         wh[i] = 0;
     __syncthreads();
-    int32_t ex = inc - mine;
-    int32_t total = 0;
+    constexpr int kHistBatch = 16;
+    const int G = E <= kRankThreads ? kRankThreads / E : 1;
+    for (int col = tid; col < G * E; col += kRankThreads) {
+        const int e = col % E;
+        const int g = col / E;
+        int32_t total = 0, before = 0;
+        for (int t0 = g; t0 < B; t0 += G * kHistBatch) {
+            int32_t h[kHistBatch];
 #pragma unroll
-    for (int v = 0; v < kRankWaves; ++v) {
-        ex += v < w ? wave_total[v] : 0;
-        total += wave_total[v];
-    }
+            for (int q = 0; q < kHistBatch; ++q) {
+                const int t = t0 + q * G;
+                h[q] = t < B ? tile_hist[(int64_t)t * E + e] : 0;
+            }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        const int e = tid * 4 + q;
-        if (e < E)
-            eoff[e] = ex;
-        ex += c4[q];
-    }
-    if (tid == 0)
-        eoff[E] = total;
-    __syncthreads();
-
-    // (2) block 0 publishes the offset table and the destination counts
-    if (blockIdx.x == 0) {
-        for (int e = tid; e <= E; e += kLayoutThreads)
-            expert_offsets[e] = eoff[e];
-        const int32_t el = E / R;
-        for (int r = tid; r < R; r += kLayoutThreads) {
-            dest_offsets[r] = eoff[r * el];
-            dest_counts[r] = eoff[(r + 1) * el] - eoff[r * el];
+            for (int q = 0; q < kHistBatch; ++q) {
+                total += h[q];
+                before += t0 + q * G < b ? h[q] : 0;
+            }
         }
-        if (tid == 0)
-            dest_offsets[R] = eoff[E];
-    }
-
-    // (3) stable ranks inside each wave's span, in assignment order
-    const int64_t a0 = (int64_t)blockIdx.x * kLayoutTile + (int64_t)w * kWaveSpan;
-    int32_t ev[kSteps];
-    int32_t rk[kSteps];
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-        const int64_t a = a0 + s * kWave + lane;
-        ev[s] = a < TK ? idx[a] : -1;
-    }
-    int32_t *my_wh = wh + w * E;
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-        const int32_t e = ev[s];
-        const bool valid = (uint32_t)e < (uint32_t)E;
-        uint64_t same = ballot64(valid);
-        for (int b = 0; b < nbits; ++b) {
-            const bool bit = (e >> b) & 1;
-            const uint64_t ones = ballot64(bit);
-            same &= bit ? ones : ~ones;
-        }
-        const int32_t below = (int32_t)count_below(same);
-        const int32_t seen = valid ? my_wh[e] : 0;
-        if (valid && below == 0)
-            my_wh[e] = seen + (int32_t)__popcll(same);
-        rk[s] = seen + below;
-        ev[s] = valid ? e : -1;
+        atomicAdd(&cnt[e], total);
+        atomicAdd(&base[e], before);
     }
     __syncthreads();
-
-    // (4) per expert: first rank of each wave = tile base + earlier waves
-    for (int e = tid; e < E; e += kLayoutThreads) {
+    for (int e = tid; e < E; e += kRankThreads) {
+        const int32_t total = cnt[e];
+        const int32_t kept = (capacity < 0 || total < capacity) ? total : capacity;
+        cnt[e] = kept;
+        if (b == 0) {
+            expert_demand[e] = total;
+            expert_counts[e] = kept;
+        }
+    }
+    __syncthreads();
+    block_scan_counts<kRankThreads>(cnt, E, eoff, wave_total);
+    const int64_t begin = (int64_t)b * tile;
+    const int64_t end = min(TK, begin + tile);
+    int64_t lo, hi;
+    wave_span(begin, end, w, kRankWaves, lo, hi);
+    count_range(idx, lo, hi, lane_id(), kWave, E, wh + w * E);  // pass A
+    __syncthreads();
+    if (b == 0)
+        publish_offsets(eoff, E, R, expert_offsets, dest_counts, dest_offsets);
+    for (int e = tid; e < E; e += kRankThreads) {
         int32_t run = base[e];
-#pragma unroll
         for (int v = 0; v < kRankWaves; ++v) {
             const int32_t c = wh[v * E + e];
             wh[v * E + e] = run;
@@ -201,27 +322,29 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_rank_kernel(
         }
     }
     __syncthreads();
-
-    // (5) positions, drops and the inverse map
-#pragma unroll
-    for (int s = 0; s < kSteps; ++s) {
-        const int64_t a = a0 + s * kWave + lane;
-        if (a < TK) {
-            const int32_t e = ev[s];
-            int32_t p = -1;
-            if (e >= 0) {
-                const int32_t r = my_wh[e] + rk[s];
-                if (capacity < 0 || r < capacity)
-                    p = eoff[e] + r;
-            }
-            pos[a] = p;
-            if (p >= 0 && send_src)
-                send_src[p] = (int32_t)((uint32_t)a / (uint32_t)k);
-        }
-    }
+    rank_range(idx, lo, hi, k, E, capacity, nbits, wh + w * E, eoff, pos, send_src);  // pass B
 }
 
 }  // namespace
+
+LayoutPlan layout_plan(int64_t TK, int32_t E)
+{
+    LayoutPlan p;
+    p.small = TK <= kSmallAssignments && E <= kSmallMaxExperts;
+    if (p.small || TK == 0) {
+        p.tile = 0;
+        p.tiles = 0;
+        return p;
+    }
+    int64_t tile = kLayoutTile;
+    if ((TK + tile - 1) / tile > kMaxTiles) {
+        const int64_t per = (TK + kMaxTiles - 1) / kMaxTiles;
+        tile = (per + kLayoutThreads - 1) / kLayoutThreads * kLayoutThreads;
+    }
+    p.tile = tile;
+    p.tiles = (TK + tile - 1) / tile;
+    return p;
+}
 
 hipError_t launch_dispatch_layout(const int32_t *topk_idx, int64_t T, int32_t E, int32_t k,
                                   int32_t R, int32_t capacity, int32_t *expert_demand,
@@ -230,27 +353,42 @@ hipError_t launch_dispatch_layout(const int32_t *topk_idx, int64_t T, int32_t E,
                                   int32_t *send_src, int32_t *tile_hist, hipStream_t stream)
 {
     const int64_t TK = T * (int64_t)k;
-    const int64_t B = layout_tiles(TK);
     int nbits = 0;
     while ((1 << nbits) < E)
         ++nbits;
-    if (B > 0) {
-        hipLaunchKernelGGL(layout_count_kernel, dim3((unsigned)B), dim3(kLayoutThreads),
-                           E * sizeof(int32_t), stream, topk_idx, TK, E, tile_hist);
+    const LayoutPlan plan = layout_plan(TK, E);
+    if (plan.small) {
+        const size_t lds = (size_t)(kSmallWaves * E + E + E + 1) * sizeof(int32_t);
+        hipLaunchKernelGGL(layout_small_kernel, dim3(1), dim3(kSmallThreads), lds, stream,
+                           topk_idx, TK, k, E, R, capacity, nbits, expert_demand, expert_counts,
+                           expert_offsets, dest_counts, dest_offsets, pos, send_src);
+        return hipGetLastError();
+    }
+    if (plan.tiles > 0) {
+        hipLaunchKernelGGL(layout_count_kernel, dim3((unsigned)plan.tiles), dim3(kLayoutThreads),
+                           E * sizeof(int32_t), stream, topk_idx, TK, plan.tile, E, tile_hist);
         hipError_t err = hipGetLastError();
         if (err != hipSuccess)
             return err;
     }
-    hipLaunchKernelGGL(layout_scan_kernel, dim3((unsigned)((E + kWave - 1) / kWave)),
-                       dim3(kScanWaves * kWave), 0, stream, tile_hist, B, E, capacity,
-                       expert_demand, expert_counts);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess)
-        return err;
-    const size_t lds = (size_t)(E + 1 + E + kRankWaves * E) * sizeof(int32_t);
-    hipLaunchKernelGGL(layout_rank_kernel, dim3((unsigned)(B > 0 ? B : 1)), dim3(kLayoutThreads),
-                       lds, stream, topk_idx, TK, B, k, E, R, capacity, nbits, tile_hist,
-                       expert_counts, expert_offsets, dest_counts, dest_offsets, pos, send_src);
+    // with no assignments a single block still writes the (zero) counts;
+    // 16 waves per block when the LDS rows fit (E <= 512), else 8
+    const dim3 grid((unsigned)(plan.tiles > 0 ? plan.tiles : 1));
+    if (E <= kSmallMaxExperts) {
+        constexpr int threads = 1024;
+        const size_t lds = (size_t)((threads / kWave) * E + 3 * E + 1) * sizeof(int32_t);
+        hipLaunchKernelGGL(layout_rank_kernel<threads>, grid, dim3(threads), lds, stream, topk_idx,
+                           TK, plan.tile, (int32_t)plan.tiles, k, E, R, capacity, nbits, tile_hist,
+                           expert_demand, expert_counts, expert_offsets, dest_counts, dest_offsets,
+                           pos, send_src);
+    } else {
+        constexpr int threads = 512;
+        const size_t lds = (size_t)((threads / kWave) * E + 3 * E + 1) * sizeof(int32_t);
+        hipLaunchKernelGGL(layout_rank_kernel<threads>, grid, dim3(threads), lds, stream, topk_idx,
+                           TK, plan.tile, (int32_t)plan.tiles, k, E, R, capacity, nbits, tile_hist,
+                           expert_demand, expert_counts, expert_offsets, dest_counts, dest_offsets,
+                           pos, send_src);
+    }
     return hipGetLastError();
 }
 

@@ -7,17 +7,23 @@
 // router scores); aicassindra "gpu_moe_all_to_all", "Two collectives per
 // layer" (gate weights scale the returning outputs).
 //
-// Layout on gfx950: lane l of the wave owns experts l, l + 64, l + 128, ...
-// (KPL = ceil(E / 64) registers), so each load instruction reads 256
-// contiguous bytes of the logit row. Scores become order-preserving 32-bit
-// keys. Each lane keeps its two best remaining (key, id, logit) candidates;
-// a selection round is a wave-wide 32-bit maximum (DPP within rows, then
-// four readlanes on the scalar unit), a ballot of the lanes holding that
-// key, and -- only when two lanes tie on the key -- a wave minimum of their
-// expert ids, so ties go to the smaller id. The winning lane pops its
-// candidate and rescans its registers only when both candidates are used
-// up. Round j's id and logit are kept by lane j, so lanes
-// 0..k-1 finish with the softmax and one coalesced row of ids and weights.
+// Layout on gfx950. When E % 4 == 0 and the rows are 16-byte aligned, lane
+// l of the wave owns experts 4l..4l+3, 256 + 4l.., ... and reads them with
+// 16-byte non-temporal loads (one instruction covers 1 KiB of the row);
+// otherwise lane l owns experts l, l + 64, ... with 4-byte loads. On MI355X
+// the 16-byte form reads the logits at ~6.9 TB/s against ~2 TB/s for the
+// 4-byte form, which made the load phase the bottleneck of this kernel.
+// Either way a lane's slots are in ascending expert order. Scores become
+// order-preserving 32-bit keys and each lane keeps its two best remaining
+// (key, id) candidates, built without branches. A selection round is a
+// wave-wide 32-bit maximum by DPP (six fused max steps, one readlane), a
+// ballot of the lanes holding that key and -- only when two lanes hold an
+// equal key -- a DPP minimum of their ids, so ties go to the smaller id.
+// The winning lane pops its candidate; it rescans its registers only once
+// both candidates are used (rare: a lane must win three of the k rounds).
+// Lane j keeps round j's id; at the end lanes 0..k-1 gather their unbiased
+// logits from the row (still in cache), take the softmax and write one
+// coalesced row of ids and weights.
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -26,6 +32,8 @@ namespace {
 
 constexpr int kRouteThreads = 256;
 constexpr int kTokensPerBlock = kRouteThreads / kWave;
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Order-preserving map of a float score onto uint32: larger key = higher
 // rank. The caller adds +0.0f first, which turns -0 into +0 and leaves
@@ -38,21 +46,24 @@ __device__ __forceinline__ uint32_t score_key(float s)
     return s != s ? 1u : k;
 }
 
-struct Candidate {
-    uint32_t key, id;
-    float logit;
-};
-
-__device__ __forceinline__ bool ranks_below(uint32_t key, uint32_t id, uint32_t ref_key,
-                                            uint32_t ref_id)
+// Expert id held in slot i of lane `lane`, and the lane that holds expert e.
+template <int VEC>
+__device__ __forceinline__ uint32_t slot_id(int i, int lane)
 {
-    return key < ref_key || (key == ref_key && id > ref_id);
+    return VEC == 4 ? (uint32_t)((i / 4) * 4 * kWave + 4 * lane + (i % 4))
+                    : (uint32_t)(i * kWave + lane);
+}
+template <int VEC>
+__device__ __forceinline__ int owner_lane(uint32_t e)
+{
+    return VEC == 4 ? (int)((e >> 2) & (kWave - 1)) : (int)(e & (kWave - 1));
 }
 
-template <int KPL>
+// NSLOT keys per lane; VEC = 4 (16-byte loads) or 1 (4-byte loads)
+template <int NSLOT, int VEC, bool NORMALIZE>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int64_t T, int32_t E,
-    int32_t k, int normalize, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w)
+    int32_t k, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t t = (int64_t)blockIdx.x * kTokensPerBlock + (threadIdx.x / kWave);
@@ -60,110 +71,122 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
         return;  // t is uniform across the wave: whole waves leave together
     const float *row = logits + t * E;
 
-    uint32_t key[KPL];
-    float logit[KPL];
+    uint32_t key[NSLOT];
+    if (VEC == 4) {
+        const f32x4 *row4 = reinterpret_cast<const f32x4 *>(row);
+        const f32x4 *bias4 = reinterpret_cast<const f32x4 *>(bias);
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-        const int e = i * kWave + lane;
-        if (e < E) {
-            const float v = row[e];
-            logit[i] = v;
-            key[i] = score_key((bias ? v + bias[e] : v) + 0.0f);
-        } else {
-            logit[i] = 0.f;
-            key[i] = 0u;
+        for (int g = 0; g < NSLOT / 4; ++g) {
+            if (g * 4 * kWave + 4 * lane < E) {
+                const f32x4 v = __builtin_nontemporal_load(row4 + g * kWave + lane);
+                const f32x4 b = bias ? bias4[g * kWave + lane] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    key[4 * g + c] = score_key((bias ? v[c] + b[c] : v[c]) + 0.0f);
+            } else {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    key[4 * g + c] = 0u;  // padding ranks below everything
+            }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NSLOT; ++i) {
+            const int e = i * kWave + lane;
+            if (e < E) {
+                const float v = row[e];
+                key[i] = score_key((bias ? v + bias[e] : v) + 0.0f);
+            } else {
+                key[i] = 0u;  // padding ranks below everything, NaN included
+            }
         }
     }
 
     // the lane's two best entries; ascending i is ascending id, so strict
     // comparisons keep the smaller id first among equal keys
-    Candidate c1 = {0u, 0xFFFFFFFFu, 0.f}, c2 = {0u, 0xFFFFFFFFu, 0.f};
+    uint32_t c1k = key[0], c1i = slot_id<VEC>(0, lane), c2k = 0u, c2i = 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 0; i < KPL; ++i) {
-        const Candidate c = {key[i], (uint32_t)(i * kWave + lane), logit[i]};
-        if (c.key > c1.key) {
-            c2 = c1;
-            c1 = c;
-        } else if (c.key > c2.key) {
-            c2 = c;
-        }
+    for (int i = 1; i < NSLOT; ++i) {
+        const uint32_t kk = key[i], id = slot_id<VEC>(i, lane);
+        const bool gt1 = kk > c1k, gt2 = kk > c2k;
+        c2k = gt1 ? c1k : (gt2 ? kk : c2k);
+        c2i = gt1 ? c1i : (gt2 ? id : c2i);
+        c1k = gt1 ? kk : c1k;
+        c1i = gt1 ? id : c1i;
     }
 
     uint32_t my_e = 0;
-    float my_l = 0.f;
-    float m = -INFINITY;  // max unbiased logit among the selected
     for (int j = 0; j < k; ++j) {
-        const uint32_t best = wave_max_u32(c1.key);
-        const uint64_t holders = ballot64(c1.key == best);
+        const uint32_t best = wave_max_u32(c1k);
+        const uint64_t holders = ballot64(c1k == best);
         int owner;
         uint32_t ew;
         if (__popcll(holders) == 1) {
             owner = __ffsll((unsigned long long)holders) - 1;
-            ew = readlane_u32(c1.id, owner);
+            ew = readlane_u32(c1i, owner);
         } else {  // several lanes hold an equal key: the smallest id wins
-            ew = wave_min_u32(c1.key == best ? c1.id : 0xFFFFFFFFu);
-            owner = (int)(ew & (kWave - 1));
+            ew = wave_min_u32(c1k == best ? c1i : 0xFFFFFFFFu);
+            owner = owner_lane<VEC>(ew);
         }
-        const float lw = __uint_as_float(readlane_u32(__float_as_uint(c1.logit), owner));
-        if (lane == j) {
-            my_e = ew;
-            my_l = lw;
-        }
-        m = fmaxf(m, lw);
-        if (lane == owner) {
-            const uint32_t gone_key = c1.key, gone_id = c1.id;
-            c1 = c2;
-            c2 = {0u, 0xFFFFFFFFu, 0.f};
-            if (c1.key == 0u) {
-                // both candidates used: rescan the entries ranked below the
-                // last one taken from this lane
+        my_e = lane == j ? ew : my_e;
+        const bool own = lane == owner;
+        const uint32_t gone_k = c1k, gone_i = c1i;
+        c1k = own ? c2k : c1k;
+        c1i = own ? c2i : c1i;
+        c2k = own ? 0u : c2k;
+        if (own && c1k == 0u) {
+            // both candidates used: rescan the entries ranked below the last
+            // one taken from this lane
+            c2i = 0xFFFFFFFFu;
 #pragma unroll
-                for (int i = 0; i < KPL; ++i) {
-                    const Candidate c = {key[i], (uint32_t)(i * kWave + lane), logit[i]};
-                    if (!ranks_below(c.key, c.id, gone_key, gone_id))
-                        continue;
-                    if (c.key > c1.key) {
-                        c2 = c1;
-                        c1 = c;
-                    } else if (c.key > c2.key) {
-                        c2 = c;
-                    }
-                }
+            for (int i = 0; i < NSLOT; ++i) {
+                const uint32_t id = slot_id<VEC>(i, lane);
+                const uint32_t kk =
+                    (key[i] < gone_k || (key[i] == gone_k && id > gone_i)) ? key[i] : 0u;
+                const bool gt1 = kk > c1k, gt2 = kk > c2k;
+                c2k = gt1 ? c1k : (gt2 ? kk : c2k);
+                c2i = gt1 ? c1i : (gt2 ? id : c2i);
+                c1k = gt1 ? kk : c1k;
+                c1i = gt1 ? id : c1i;
             }
         }
     }
 
+    // unbiased logits of the selected experts, straight from the row
+    const bool mine = lane < k;
+    const float my_l = mine ? row[my_e] : -INFINITY;
     float w;
-    if (normalize) {
-        const float u = lane < k ? expf(my_l - m) : 0.f;
+    if (NORMALIZE) {
+        const float m = wave_max_f32_dpp(my_l);
+        const float u = mine ? expf(my_l - m) : 0.f;
         w = u / wave_sum_f32_dpp(u);
     } else {
         float lm = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < KPL; ++i)
-            if (i * kWave + lane < E)
-                lm = fmaxf(lm, logit[i]);
+        for (int e = lane; e < E; e += kWave)
+            lm = fmaxf(lm, row[e]);
         const float M = wave_max_f32_dpp(lm);
         float part = 0.f;
-#pragma unroll
-        for (int i = 0; i < KPL; ++i)
-            if (i * kWave + lane < E)
-                part += expf(logit[i] - M);
-        w = (lane < k ? expf(my_l - M) : 0.f) / wave_sum_f32_dpp(part);
+        for (int e = lane; e < E; e += kWave)
+            part += expf(row[e] - M);
+        w = (mine ? expf(my_l - M) : 0.f) / wave_sum_f32_dpp(part);
     }
-    if (lane < k) {
+    if (mine) {
         topk_idx[t * k + lane] = (int32_t)my_e;
         topk_w[t * k + lane] = w;
     }
 }
 
-template <int KPL>
-hipError_t launch_kpl(const float *logits, const float *bias, int64_t T, int32_t E, int32_t k,
-                      bool normalize, int32_t *topk_idx, float *topk_w, hipStream_t stream)
+template <int NSLOT, int VEC>
+hipError_t launch_slots(const float *logits, const float *bias, int64_t T, int32_t E, int32_t k,
+                        bool normalize, int32_t *topk_idx, float *topk_w, hipStream_t stream)
 {
     const dim3 grid((unsigned)((T + kTokensPerBlock - 1) / kTokensPerBlock));
-    hipLaunchKernelGGL(route_topk_kernel<KPL>, grid, dim3(kRouteThreads), 0, stream, logits, bias,
-                       T, E, k, normalize ? 1 : 0, topk_idx, topk_w);
+    if (normalize)
+        hipLaunchKernelGGL((route_topk_kernel<NSLOT, VEC, true>), grid, dim3(kRouteThreads), 0,
+                           stream, logits, bias, T, E, k, topk_idx, topk_w);
+    else
+        hipLaunchKernelGGL((route_topk_kernel<NSLOT, VEC, false>), grid, dim3(kRouteThreads), 0,
+                           stream, logits, bias, T, E, k, topk_idx, topk_w);
     return hipGetLastError();
 }
 
@@ -173,10 +196,25 @@ hipError_t launch_route_topk(const float *logits, const float *bias, int64_t T, 
                              int32_t k, bool normalize, int32_t *topk_idx, float *topk_w,
                              hipStream_t stream)
 {
+    const bool vec4 = E % 4 == 0 && (uintptr_t)logits % 16 == 0 && (uintptr_t)bias % 16 == 0;
+    if (vec4) {
+        switch ((E + 4 * kWave - 1) / (4 * kWave)) {
+        case 1:
+            return launch_slots<4, 4>(logits, bias, T, E, k, normalize, topk_idx, topk_w, stream);
+        case 2:
+            return launch_slots<8, 4>(logits, bias, T, E, k, normalize, topk_idx, topk_w, stream);
+        case 3:
+            return launch_slots<12, 4>(logits, bias, T, E, k, normalize, topk_idx, topk_w, stream);
+        case 4:
+            return launch_slots<16, 4>(logits, bias, T, E, k, normalize, topk_idx, topk_w, stream);
+        default:
+            return hipErrorInvalidValue;
+        }
+    }
     switch ((E + kWave - 1) / kWave) {
 #define MOE_ROUTE_CASE(n) \
     case n:               \
-        return launch_kpl<n>(logits, bias, T, E, k, normalize, topk_idx, topk_w, stream);
+        return launch_slots<n, 1>(logits, bias, T, E, k, normalize, topk_idx, topk_w, stream);
         MOE_ROUTE_CASE(1)
         MOE_ROUTE_CASE(2)
         MOE_ROUTE_CASE(3)

@@ -63,9 +63,14 @@ def test_route_validation(moe):
 
 
 def test_workspace_size(moe):
-    # one E-wide int32 histogram per tile of 2048 assignments
-    assert moe.moe_layout_workspace_size(32768, 512, 10, 64) == 160 * 512 * 4
-    assert moe.moe_layout_workspace_size(256, 16, 2, 4) == 1 * 16 * 4
+    # one E-wide int32 histogram per tile: tiles of 2048 assignments, at most
+    # 128 of them; up to 4096 assignments (E <= 512) need no workspace
+    assert moe.moe_layout_workspace_size(32768, 512, 10, 64) == 128 * 512 * 4
+    assert moe.moe_layout_workspace_size(8192, 64, 8, 8) == 32 * 64 * 4
+    assert moe.moe_layout_workspace_size(4096, 384, 8, 64) == 16 * 384 * 4
+    assert moe.moe_layout_workspace_size(512, 384, 8, 64) == 0
+    assert moe.moe_layout_workspace_size(256, 16, 2, 4) == 0
+    assert moe.moe_layout_workspace_size(256, 1024, 2, 4) == 1 * 1024 * 4
     assert moe.moe_layout_workspace_size(0, 16, 2, 4) == 0
     with pytest.raises(moe.MoeError):
         moe.moe_layout_workspace_size(256, 16, 2, 3)      # E % R != 0
@@ -88,9 +93,12 @@ def test_layout_validation(moe):
     assert _layout(lib, idx=None) == moe.MOE_ERR_INVALID_ARG
     assert _layout(lib, pos=MIS) == moe.MOE_ERR_INVALID_ARG
     assert _layout(lib, out=None) == moe.MOE_ERR_INVALID_ARG
-    assert _layout(lib, ws=None) == moe.MOE_ERR_WORKSPACE
-    assert _layout(lib, ws_bytes=63) == moe.MOE_ERR_WORKSPACE
-    assert _layout(lib, ws=FAKE + 8) == moe.MOE_ERR_WORKSPACE
+    # 65536 assignments take the tiled layout: 32 tiles x 64 experts x 4 bytes
+    big = dict(T=8192, E=64, k=8, R=8)
+    assert moe.moe_layout_workspace_size(8192, 64, 8, 8) == 8192
+    assert _layout(lib, ws=None, **big) == moe.MOE_ERR_WORKSPACE
+    assert _layout(lib, ws_bytes=8191, **big) == moe.MOE_ERR_WORKSPACE
+    assert _layout(lib, ws=FAKE + 8, **big) == moe.MOE_ERR_WORKSPACE
 
 
 def test_permute_and_combine_validation(moe):

@@ -245,6 +245,12 @@ SHAPES = [
     (3000, 128, 40, 3, 1, 100),   # R = 1
     (70001, 16, 32, 8, 8, -1),    # 274 tiles: several tiles per scan wave
     (2048, 64, 8, 2, 2, 0),       # capacity 0 drops everything
+    (1500, 64, 250, 6, 5, -1),    # E % 4 != 0: 4-byte route loads
+    (200, 32, 13, 3, 13, -1),     # E % 4 != 0, one expert per destination
+    (512, 16, 64, 8, 8, 70),      # 4096 assignments: the one-block layout, capacity
+    (513, 16, 64, 8, 8, 70),      # 4104 assignments: the tiled layout, capacity
+    (20000, 16, 64, 4, 8, 900),   # tiled layout, capacity, several tiles
+    (1000, 32, 600, 4, 6, 50),    # E > 512 takes the tiled layout at any size
 ]
 
 
@@ -313,9 +319,10 @@ def test_round_robin_indices(moe):
     assert np.all(got["expert_demand"] == per)
 
 
-def test_zero_tokens(moe):
-    say("zero tokens")
-    E, k, R, H = 16, 2, 4, 64
+@pytest.mark.parametrize("E", [16, 1024])
+def test_zero_tokens(moe, E):
+    say(f"zero tokens E={E}")
+    k, R, H = 2, 4, 64
     idx, wt = moe.moe_route_topk(torch.empty((0, E), device=DEV), None, k)
     L = moe.moe_dispatch_layout(idx, E, R, -1)
     send = moe.moe_dispatch_permute(torch.empty((0, H), dtype=torch.bfloat16, device=DEV), L["pos"], 0)
@@ -374,3 +381,22 @@ def test_reproducible(moe):
         outs.append([t.cpu() for t in (idx, wt, L["pos"], L["send_src"][:N], send[:N], out)])
     for a, b in zip(*outs):
         assert np.array_equal(a.contiguous().view(torch.uint8).numpy(), b.contiguous().view(torch.uint8).numpy())
+
+
+@pytest.mark.parametrize("E", [512, 384])
+def test_route_misaligned_rows(moe, E):
+    """Logit rows that are only 4-byte aligned take the 4-byte load path."""
+    T, k = 777, 8
+    r = np.random.default_rng(E)
+    logits = r.standard_normal((T, E), dtype=np.float32)
+    bias = r.uniform(-0.1, 0.1, E).astype(np.float32)
+    say(f"route misaligned rows T={T} E={E} k={k}")
+    flat = torch.zeros(T * E + 1, dtype=torch.float32, device=DEV)
+    flat[1:] = up(logits.ravel())
+    view = flat[1:].view(T, E)
+    assert view.data_ptr() % 16 != 0
+    idx, wt = moe.moe_route_topk(view, up(bias), k)
+    torch.cuda.synchronize()
+    o_idx, o_w = oracle.route_topk(logits, bias, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), o_idx)
+    assert np.all(np.abs(wt.cpu().numpy() - o_w) <= weight_tolerance(logits, o_idx, o_w, k))
