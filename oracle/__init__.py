@@ -51,13 +51,14 @@ def _load():
         P = ctypes.c_void_p
         i32, i64 = ctypes.c_int32, ctypes.c_int64
         lib.oracle_route_topk.argtypes = [P, P, i64, i32, i32, i32, P, P]
+        lib.oracle_route_topk_grouped.argtypes = [P, P, i64, i32, i32, i32, i32, i32, P, P]
         lib.oracle_dispatch_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P]
         lib.oracle_dispatch_permute.argtypes = [P, P, i64, i32, i32, P, i64]
         lib.oracle_combine_reduce.argtypes = [P, i64, P, P, P, P, i64, i32, i32, P, i64, P]
         lib.oracle_bf16_round.argtypes = [ctypes.c_double]
         lib.oracle_bf16_round.restype = ctypes.c_uint16
         lib.oracle_bf16_round_array.argtypes = [P, i64, P]
-        for f in ("oracle_route_topk", "oracle_dispatch_layout",
+        for f in ("oracle_route_topk", "oracle_route_topk_grouped", "oracle_dispatch_layout",
                   "oracle_dispatch_permute", "oracle_combine_reduce"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
@@ -85,6 +86,23 @@ def route_topk(logits: np.ndarray, bias: Optional[np.ndarray], k: int,
                                    1 if normalize else 0, _ptr(idx), _ptr(w))
     if rc != 0:
         raise ValueError("oracle_route_topk rejected its arguments")
+    return idx, w
+
+
+def route_topk_grouped(logits: np.ndarray, bias: Optional[np.ndarray], k: int,
+                       n_groups: int, topk_groups: int, normalize: bool = True):
+    """Group-limited top-k: the best topk_groups expert groups (ranked by their
+    best score), then the top k experts inside them; see
+    oracle_route_topk_grouped."""
+    logits = _c(logits, np.float32)
+    T, E = logits.shape
+    bias = None if bias is None else _c(bias, np.float32)
+    idx = np.empty((T, k), np.int32)
+    w = np.empty((T, k), np.float64)
+    rc = _load().oracle_route_topk_grouped(_ptr(logits), _ptr(bias), T, E, k, n_groups,
+                                           topk_groups, 1 if normalize else 0, _ptr(idx), _ptr(w))
+    if rc != 0:
+        raise ValueError("oracle_route_topk_grouped rejected its arguments")
     return idx, w
 
 

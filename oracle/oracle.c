@@ -121,14 +121,53 @@ static int ranks_above(float a, int ia, float b, int ib)
     return ia < ib;
 }
 
+/* Selection scores of one token: one float add per expert. */
+static void biased_scores(const float *row, const float *bias, int32_t E, float *s)
+{
+    for (int32_t e = 0; e < E; ++e)
+        s[e] = bias ? row[e] + bias[e] : row[e];
+}
+
 /*
- * For each token t: score s_e = logit[t][e] + bias[e] in float; select the k
- * experts with the highest scores, in descending rank order. Gate weights
- * use the unbiased logits of the selected experts only:
+ * Gate weights of one token from its UNBIASED logits `row` and the k
+ * selected experts:
  *   normalize != 0: w_j = exp(l_j - m) / sum_i exp(l_i - m) over the k
  *                   selected (softmax renormalised over the selection);
  *   normalize == 0: w_j = exp(l_j - M) / sum over all E experts of
  *                   exp(l_e - M) (full softmax, not renormalised).
+ */
+static void gate_weights(const float *row, const int32_t *idx, int32_t E, int32_t k,
+                         int32_t normalize, double *w)
+{
+    if (normalize) {
+        double m = -INFINITY;
+        for (int32_t j = 0; j < k; ++j)
+            if ((double)row[idx[j]] > m)
+                m = (double)row[idx[j]];
+        double sum = 0.0;
+        for (int32_t j = 0; j < k; ++j) {
+            w[j] = exp((double)row[idx[j]] - m);
+            sum += w[j];
+        }
+        for (int32_t j = 0; j < k; ++j)
+            w[j] /= sum;
+    } else {
+        double m = -INFINITY;
+        for (int32_t e = 0; e < E; ++e)
+            if ((double)row[e] > m)
+                m = (double)row[e];
+        double sum = 0.0;
+        for (int32_t e = 0; e < E; ++e)
+            sum += exp((double)row[e] - m);
+        for (int32_t j = 0; j < k; ++j)
+            w[j] = exp((double)row[idx[j]] - m) / sum;
+    }
+}
+
+/*
+ * For each token t: score s_e = logit[t][e] + bias[e] in float; select the k
+ * experts with the highest scores, in descending rank order; gate weights
+ * come from the unbiased logits of the selected experts (gate_weights).
  * Returns 0, or -1 on bad sizes or allocation failure.
  */
 int oracle_route_topk(const float *logits, const float *bias, int64_t T,
@@ -146,10 +185,9 @@ int oracle_route_topk(const float *logits, const float *bias, int64_t T,
     }
     for (int64_t t = 0; t < T; ++t) {
         const float *row = logits + t * (int64_t)E;
-        for (int32_t e = 0; e < E; ++e) {
-            s[e] = bias ? row[e] + bias[e] : row[e];
+        biased_scores(row, bias, E, s);
+        for (int32_t e = 0; e < E; ++e)
             taken[e] = 0;
-        }
         int32_t *idx = topk_idx + t * (int64_t)k;
         for (int32_t j = 0; j < k; ++j) {
             int32_t best = -1;
@@ -162,33 +200,95 @@ int oracle_route_topk(const float *logits, const float *bias, int64_t T,
             taken[best] = 1;
             idx[j] = best;
         }
-        double *w = topk_w + t * (int64_t)k;
-        if (normalize) {
-            double m = -INFINITY;
-            for (int32_t j = 0; j < k; ++j)
-                if ((double)row[idx[j]] > m)
-                    m = (double)row[idx[j]];
-            double sum = 0.0;
-            for (int32_t j = 0; j < k; ++j) {
-                w[j] = exp((double)row[idx[j]] - m);
-                sum += w[j];
-            }
-            for (int32_t j = 0; j < k; ++j)
-                w[j] /= sum;
-        } else {
-            double m = -INFINITY;
-            for (int32_t e = 0; e < E; ++e)
-                if ((double)row[e] > m)
-                    m = (double)row[e];
-            double sum = 0.0;
-            for (int32_t e = 0; e < E; ++e)
-                sum += exp((double)row[e] - m);
-            for (int32_t j = 0; j < k; ++j)
-                w[j] = exp((double)row[idx[j]] - m) / sum;
-        }
+        gate_weights(row, idx, E, k, normalize, topk_w + t * (int64_t)k);
     }
     free(s);
     free(taken);
+    return 0;
+}
+
+/*
+ * Group-limited routing. Experts form n_groups contiguous groups of
+ * E / n_groups (destination groups, e.g. nodes). Each token may use at most
+ * topk_groups of them: rank every group by its best expert score (the same
+ * order as the expert selection, so ties go to the lower group id), keep the
+ * best topk_groups groups, then select the k best experts inside them and
+ * compute the weights exactly as oracle_route_topk does.
+ *
+ * Source: ai-from-scratch "19. All-to-all", "DeepSeek's numbers" (each
+ * token limited to at most 4 nodes) and the closing section (node-limited
+ * routing as an architectural constraint); zenaique Q&A
+ * "moe-hide-alltoall-techniques" (node-limited routing caps cross-node
+ * traffic). The pages do not define the group score; the group's best
+ * biased score is the plainest reading.
+ * Returns 0, or -1 on bad sizes.
+ */
+int oracle_route_topk_grouped(const float *logits, const float *bias, int64_t T,
+                              int32_t E, int32_t k, int32_t n_groups,
+                              int32_t topk_groups, int32_t normalize,
+                              int32_t *topk_idx, double *topk_w)
+{
+    if (T < 0 || E <= 0 || k <= 0 || n_groups <= 0 || E % n_groups != 0 ||
+        topk_groups <= 0 || topk_groups > n_groups ||
+        k > topk_groups * (E / n_groups))
+        return -1;
+    const int32_t gsize = E / n_groups;
+    float *s = (float *)malloc((size_t)E * sizeof(float));
+    char *taken = (char *)malloc((size_t)E);
+    char *gsel = (char *)malloc((size_t)n_groups);
+    int32_t *gbest = (int32_t *)malloc((size_t)n_groups * sizeof(int32_t));
+    if (!s || !taken || !gsel || !gbest) {
+        free(s);
+        free(taken);
+        free(gsel);
+        free(gbest);
+        return -1;
+    }
+    for (int64_t t = 0; t < T; ++t) {
+        const float *row = logits + t * (int64_t)E;
+        biased_scores(row, bias, E, s);
+        /* best expert of each group */
+        for (int32_t g = 0; g < n_groups; ++g) {
+            int32_t best = g * gsize;
+            for (int32_t e = g * gsize + 1; e < (g + 1) * gsize; ++e)
+                if (ranks_above(s[e], e, s[best], best))
+                    best = e;
+            gbest[g] = best;
+            gsel[g] = 0;
+        }
+        /* the topk_groups groups whose best experts rank highest; comparing
+         * the best experts' (score, id) pairs orders groups by score with
+         * ties to the lower group, since ids grow with the group */
+        for (int32_t m = 0; m < topk_groups; ++m) {
+            int32_t pick = -1;
+            for (int32_t g = 0; g < n_groups; ++g) {
+                if (gsel[g])
+                    continue;
+                if (pick < 0 || ranks_above(s[gbest[g]], gbest[g], s[gbest[pick]], gbest[pick]))
+                    pick = g;
+            }
+            gsel[pick] = 1;
+        }
+        for (int32_t e = 0; e < E; ++e)
+            taken[e] = !gsel[e / gsize];   /* experts outside the groups are out */
+        int32_t *idx = topk_idx + t * (int64_t)k;
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t best = -1;
+            for (int32_t e = 0; e < E; ++e) {
+                if (taken[e])
+                    continue;
+                if (best < 0 || ranks_above(s[e], e, s[best], best))
+                    best = e;
+            }
+            taken[best] = 1;
+            idx[j] = best;
+        }
+        gate_weights(row, idx, E, k, normalize, topk_w + t * (int64_t)k);
+    }
+    free(s);
+    free(taken);
+    free(gsel);
+    free(gbest);
     return 0;
 }
 

@@ -18,9 +18,10 @@ PIN_TESTS = ["tests/test_oracle_route.py", "tests/test_oracle_layout.py", "tests
 MUTATIONS = {
     "tie_break_to_higher_id": ("    return ia < ib;\n", "    return ia > ib;\n"),
     "nan_ranks_on_top": ("    if (!na && nb)\n        return 1;", "    if (!na && nb)\n        return 0;"),
-    "weights_from_biased_scores": ("                w[j] = exp((double)row[idx[j]] - m);",
-                                   "                w[j] = exp((double)s[idx[j]] - m);"),
-    "weights_not_normalised": ("                w[j] /= sum;", "                w[j] /= 1.0;"),
+    # the first call is the plain router's (the grouped router makes the second)
+    "weights_from_biased_scores": ("gate_weights(row, idx, E, k, normalize,", "gate_weights(s, idx, E, k, normalize,", "first"),
+    "grouped_weights_from_biased_scores": ("gate_weights(row, idx, E, k, normalize,", "gate_weights(s, idx, E, k, normalize,", "last"),
+    "weights_not_normalised": ("            w[j] /= sum;", "            w[j] /= 1.0;"),
     "score_ignores_bias": ("s[e] = bias ? row[e] + bias[e] : row[e];", "s[e] = row[e];"),
     "capacity_off_by_one": ("if (capacity >= 0 && seen[e] >= capacity)", "if (capacity >= 0 && seen[e] > capacity)"),
     "offsets_from_demand": ("expert_offsets[e] + counts[e];", "expert_offsets[e] + demand[e];"),
@@ -34,6 +35,9 @@ MUTATIONS = {
     "combine_weight_index_reversed": ("acc += w[t * k + j] *", "acc += w[t * k + (k - 1 - j)] *"),
     "combine_keeps_dropped_term": ("                if (p < 0)\n                    continue;\n                acc",
                                    "                if (p < 0)\n                    p = 0;\n                acc"),
+    "group_score_from_worst_member": ("                if (ranks_above(s[e], e, s[best], best))\n                    best = e;\n            gbest[g] = best;",
+                                      "                if (ranks_above(s[best], best, s[e], e))\n                    best = e;\n            gbest[g] = best;"),
+    "group_mask_ignored": ("            taken[e] = !gsel[e / gsize];", "            taken[e] = 0;"),
     "bf16_ties_away_from_zero": ("double r = nearbyint(a / q) * q;", "double r = round(a / q) * q;"),
     "bf16_no_subnormal_spacing": ("if (e < -126)\n        e = -126;", "if (e < -140)\n        e = -140;"),
 }
@@ -41,11 +45,17 @@ MUTATIONS = {
 
 @pytest.mark.parametrize("name", sorted(MUTATIONS))
 def test_pins_catch_mutation(name, tmp_path):
-    old, new = MUTATIONS[name]
+    old, new, *where = MUTATIONS[name]
     src = open(SRC).read()
-    assert src.count(old) == 1, f"mutation anchor for {name} not unique/found"
+    if not where:
+        assert src.count(old) == 1, f"mutation anchor for {name} not unique/found"
+        text = src.replace(old, new)
+    else:
+        i = src.find(old) if where[0] == "first" else src.rfind(old)
+        assert i >= 0 and src.count(old) == 2, f"mutation anchor for {name} not found twice"
+        text = src[:i] + new + src[i + len(old):]
     mutated = tmp_path / "oracle_mut.c"
-    mutated.write_text(src.replace(old, new))
+    mutated.write_text(text)
     lib = tmp_path / "liboracle_mut.so"
     subprocess.run(["gcc", "-std=c11", "-O2", "-ffp-contract=off", "-fno-fast-math", "-shared",
                     "-fPIC", str(mutated), "-o", str(lib), "-lm"], check=True)

@@ -154,3 +154,82 @@ def test_golden_route(orc):
 def test_route_rejects_bad_sizes(orc):
     with pytest.raises(ValueError):
         orc.route_topk(np.zeros((2, 3), np.float32), None, 4)
+
+
+# ---------------------------------------------------------------------------
+# group-limited routing (ai-from-scratch "19. All-to-all", "DeepSeek's
+# numbers": at most 4 nodes per token)
+# ---------------------------------------------------------------------------
+
+def _sort_key(v, e):
+    # ascending sort key of the selection order: numbers before NaN, larger
+    # first, then lower id
+    return (1, 0.0, e) if math.isnan(v) else (0, -v, e)
+
+
+def _grouped_by_sorting(s, k, G, M):
+    """Reformulation with Python's sort: order groups by their best member,
+    keep M, order the allowed experts, keep k."""
+    E = len(s)
+    gs = E // G
+    best = [min(range(g * gs, (g + 1) * gs), key=lambda e: _sort_key(float(s[e]), e)) for g in range(G)]
+    groups = sorted(range(G), key=lambda g: _sort_key(float(s[best[g]]), best[g]))[:M]
+    allowed = [e for e in range(E) if e // gs in groups]
+    return sorted(allowed, key=lambda e: _sort_key(float(s[e]), e))[:k]
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_grouped_brute_force(orc, seed):
+    r = np.random.default_rng(100 + seed)
+    E = int(r.choice([4, 6, 8]))
+    G = int(r.choice([d for d in (1, 2, 3, 4, 8) if E % d == 0]))
+    M = int(r.integers(1, G + 1))
+    k = int(r.integers(1, min(M * (E // G), 3) + 1))
+    T = 4
+    logits = r.choice(VALUES, size=(T, E)).astype(np.float32)
+    bias = r.choice(np.array([0.0, 0.5, -0.5], np.float32), size=E) if seed % 2 else None
+    idx, _ = orc.route_topk_grouped(logits, bias, k, G, M)
+    for t in range(T):
+        s = logits[t] if bias is None else (logits[t] + bias).astype(np.float32)
+        assert list(idx[t]) == _grouped_by_sorting(s, k, G, M), (logits[t], bias, k, G, M)
+
+
+@pytest.mark.parametrize("T,E,k,G,M", [(64, 64, 4, 8, 2), (50, 512, 10, 8, 4), (33, 256, 8, 16, 3), (20, 384, 8, 64, 8)])
+def test_grouped_matches_numpy(orc, T, E, k, G, M):
+    r = np.random.default_rng(E + G)
+    logits = r.standard_normal((T, E), dtype=np.float32)
+    bias = r.uniform(-0.1, 0.1, E).astype(np.float32)
+    idx, w = orc.route_topk_grouped(logits, bias, k, G, M)
+    s = (logits + bias).astype(np.float32)                     # distinct finite scores
+    gmax = s.reshape(T, G, E // G).max(axis=2)
+    top_groups = np.argsort(-gmax, axis=1, kind="stable")[:, :M]
+    allowed = np.zeros((T, G), bool)
+    np.put_along_axis(allowed, top_groups, True, axis=1)
+    masked = np.where(np.repeat(allowed, E // G, axis=1), s, -np.inf)
+    ref = np.argsort(-masked, axis=1, kind="stable")[:, :k]
+    np.testing.assert_array_equal(idx, ref)
+    assert all(len(set(row // (E // G))) <= M for row in idx)
+    for t in range(T):
+        ref_w = scipy.special.softmax(logits[t].astype(np.float64)[idx[t]])
+        np.testing.assert_allclose(w[t], ref_w, rtol=1e-13)
+
+
+def test_grouped_reduces_to_plain(orc):
+    r = np.random.default_rng(8)
+    T, E, k = 40, 64, 6
+    logits = r.choice(VALUES, size=(T, E)).astype(np.float32)
+    bias = r.uniform(-1, 1, E).astype(np.float32)
+    plain = orc.route_topk(logits, bias, k)
+    for G in (1, 4, 16):                  # every group allowed
+        got = orc.route_topk_grouped(logits, bias, k, G, G)
+        np.testing.assert_array_equal(got[0], plain[0])
+        np.testing.assert_array_equal(got[1], plain[1])
+    got = orc.route_topk_grouped(logits, bias, k, E, k)   # one expert per group
+    np.testing.assert_array_equal(got[0], plain[0])
+
+
+def test_grouped_rejects_bad_sizes(orc):
+    z = np.zeros((2, 12), np.float32)
+    for k, G, M in ((2, 5, 1), (2, 4, 5), (4, 4, 1), (2, 4, 0)):
+        with pytest.raises(ValueError):
+            orc.route_topk_grouped(z, None, k, G, M)
