@@ -63,6 +63,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="rough CPU time budget of the oracle baseline")
+    p.add_argument("--route-groups", default=None, metavar="G,M",
+                   help="route with moe_route_topk_grouped: at most M of G expert groups per token")
     p.add_argument("--copy-probe-mib", type=int, default=0,
                    help="also run a plain copy kernel of this size (for counter calibration)")
     return p.parse_args()
@@ -166,6 +168,7 @@ def main():
     out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
+    groups = None if args.route_groups is None else tuple(int(v) for v in args.route_groups.split(","))
     lib = moe.lib
     P = lambda t: None if t is None else t.data_ptr()
 
@@ -175,7 +178,10 @@ def main():
 
     calls = [
         ("route", lambda: check("route", lib.moe_route_topk(
-            P(logits), P(bias), T, E, k, moe.MOE_ROUTE_NORMALIZE, P(idx), P(wt), sp))),
+            P(logits), P(bias), T, E, k, moe.MOE_ROUTE_NORMALIZE, P(idx), P(wt), sp))
+         if groups is None else check("route", lib.moe_route_topk_grouped(
+            P(logits), P(bias), T, E, k, groups[0], groups[1], moe.MOE_ROUTE_NORMALIZE, P(idx),
+            P(wt), sp))),
         ("layout", lambda: check("layout", lib.moe_dispatch_layout(
             P(idx), T, E, k, R, C, P(lay["expert_demand"]), P(lay["expert_counts"]),
             P(lay["expert_offsets"]), P(lay["dest_counts"]), P(lay["dest_offsets"]),
@@ -272,7 +278,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": w.describe(), "T": T, "H": H, "E": E, "k": k, "R": R,
+        "config": {"workload": w.describe() + ("" if groups is None else
+                                               f", at most {groups[1]} of {groups[0]} expert groups per token"),
+                   "T": T, "H": H, "E": E, "k": k, "R": R,
                    "capacity": C, "shared_expert": w.shared, "kept_rows": N, "tokens_read": T_read,
                    "bytes_per_step": total, "parallelism": "single GPU (R logical destinations)"},
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),

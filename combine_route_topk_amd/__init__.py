@@ -28,7 +28,7 @@ MOE_ERR_LAUNCH = 4
 MOE_ROUTE_NORMALIZE = 1
 MOE_COMBINE_OUT_FP32 = 1
 
-EXPORTS = ("moe_route_topk", "moe_layout_workspace_size", "moe_dispatch_layout",
+EXPORTS = ("moe_route_topk", "moe_route_topk_grouped", "moe_layout_workspace_size", "moe_dispatch_layout",
            "moe_dispatch_permute", "moe_combine_reduce", "moe_status_string")
 
 
@@ -46,6 +46,7 @@ def _load_library() -> ctypes.CDLL:
     lib = ctypes.CDLL(LIB_PATH)
     P, i32, i64, u32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32
     lib.moe_route_topk.argtypes = [P, P, i64, i32, i32, u32, P, P, P]
+    lib.moe_route_topk_grouped.argtypes = [P, P, i64, i32, i32, i32, i32, u32, P, P, P]
     lib.moe_layout_workspace_size.argtypes = [i64, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.moe_dispatch_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P,
                                         ctypes.c_size_t, P]
@@ -107,6 +108,24 @@ def moe_route_topk(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int,
     _check("moe_route_topk", lib.moe_route_topk(
         _ptr(logits, _F32, "logits", 2), _ptr(bias, _F32, "bias", 1), T, E, k,
         MOE_ROUTE_NORMALIZE if normalize else 0, _ptr(topk_idx, _I32, "topk_idx"),
+        _ptr(topk_w, _F32, "topk_w"), _stream(stream)))
+    return topk_idx, topk_w
+
+
+def moe_route_topk_grouped(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int,
+                           n_groups: int, topk_groups: int, normalize: bool = True,
+                           topk_idx: Optional[torch.Tensor] = None,
+                           topk_w: Optional[torch.Tensor] = None, stream=None):
+    """Group-limited top-k: at most topk_groups of n_groups expert groups per
+    token (see moe_route_topk_grouped)."""
+    T, E = logits.shape
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check("moe_route_topk_grouped", lib.moe_route_topk_grouped(
+        _ptr(logits, _F32, "logits", 2), _ptr(bias, _F32, "bias", 1), T, E, k, n_groups,
+        topk_groups, MOE_ROUTE_NORMALIZE if normalize else 0, _ptr(topk_idx, _I32, "topk_idx"),
         _ptr(topk_w, _F32, "topk_w"), _stream(stream)))
     return topk_idx, topk_w
 

@@ -10,6 +10,7 @@ namespace {
 constexpr int32_t kMaxE = 1024;
 constexpr int32_t kMaxK = 32;
 constexpr int32_t kMaxH = 65536;
+constexpr int32_t kMaxGroups = 64;
 constexpr int64_t kMaxAssignments = (int64_t)1 << 31;
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -75,7 +76,37 @@ moe_status_t moe_route_topk(const float *logits, const float *bias, int64_t T, i
         return MOE_ERR_INVALID_ARG;
     if (!aligned(logits, 4) || !aligned(bias, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4))
         return MOE_ERR_INVALID_ARG;
-    return from_hip(moe::launch_route_topk(logits, bias, T, E, k,
+    return from_hip(moe::launch_route_topk(logits, bias, T, E, k, 0, 0,
+                                           (flags & MOE_ROUTE_NORMALIZE) != 0, topk_idx, topk_w,
+                                           static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_route_topk_grouped(const float *logits, const float *bias, int64_t T, int32_t E,
+                                    int32_t k, int32_t n_groups, int32_t topk_groups,
+                                    uint32_t flags, int32_t *topk_idx, float *topk_w,
+                                    void *stream)
+{
+    moe_status_t s = check_tokens(T, k);
+    if (s != MOE_OK)
+        return s;
+    if ((s = check_experts(E, k)) != MOE_OK)
+        return s;
+    if (flags & ~MOE_ROUTE_NORMALIZE)
+        return MOE_ERR_INVALID_ARG;
+    if (n_groups < 1 || E % n_groups != 0 || topk_groups < 1 || topk_groups > n_groups ||
+        (int64_t)k > (int64_t)topk_groups * (E / n_groups))
+        return MOE_ERR_INVALID_ARG;
+    if (n_groups > kMaxGroups)
+        return MOE_ERR_UNSUPPORTED;
+    if (T == 0)
+        return MOE_OK;
+    if (!logits || !topk_idx || !topk_w)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(logits, 4) || !aligned(bias, 4) || !aligned(topk_idx, 4) || !aligned(topk_w, 4))
+        return MOE_ERR_INVALID_ARG;
+    // every group allowed: plain routing
+    const int32_t groups = topk_groups == n_groups ? 0 : n_groups;
+    return from_hip(moe::launch_route_topk(logits, bias, T, E, k, groups, topk_groups,
                                            (flags & MOE_ROUTE_NORMALIZE) != 0, topk_idx, topk_w,
                                            static_cast<hipStream_t>(stream)));
 }

@@ -9,9 +9,11 @@
 
 namespace moe {
 
+// n_groups == 0: plain top-k; otherwise at most topk_groups of n_groups
+// contiguous expert groups per token (n_groups <= 64).
 hipError_t launch_route_topk(const float *logits, const float *bias, int64_t T, int32_t E,
-                             int32_t k, bool normalize, int32_t *topk_idx, float *topk_w,
-                             hipStream_t stream);
+                             int32_t k, int32_t n_groups, int32_t topk_groups, bool normalize,
+                             int32_t *topk_idx, float *topk_w, hipStream_t stream);
 
 // Layout plan. Up to kSmallAssignments assignments (and E <= 512) one block
 // does the whole layout. Above that, assignments are split into at most

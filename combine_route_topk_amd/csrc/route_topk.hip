@@ -7,6 +7,11 @@
 // router scores); aicassindra "gpu_moe_all_to_all", "Two collectives per
 // layer" (gate weights scale the returning outputs).
 //
+// Group-limited routing (n_groups > 0): ai-from-scratch "19. All-to-all",
+// "DeepSeek's numbers" (each token limited to a few nodes) and the closing
+// section (node-limited routing as an architectural constraint). Groups are
+// ranked by their best biased score, the plainest reading of a group score.
+//
 // Layout on gfx950. When E % 4 == 0 and the rows are 16-byte aligned, lane
 // l of the wave owns experts 4l..4l+3, 256 + 4l.., ... and reads them with
 // 16-byte non-temporal loads (one instruction covers 1 KiB of the row);
@@ -63,7 +68,8 @@ __device__ __forceinline__ int owner_lane(uint32_t e)
 template <int NSLOT, int VEC, bool NORMALIZE>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int64_t T, int32_t E,
-    int32_t k, int32_t *__restrict__ topk_idx, float *__restrict__ topk_w)
+    int32_t k, int32_t n_groups, int32_t topk_groups, int32_t *__restrict__ topk_idx,
+    float *__restrict__ topk_w)
 {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t t = (int64_t)blockIdx.x * kTokensPerBlock + (threadIdx.x / kWave);
@@ -100,6 +106,38 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
                 key[i] = 0u;  // padding ranks below everything, NaN included
             }
         }
+    }
+
+    if (n_groups > 0) {
+        // group-limited routing: rank the n_groups contiguous expert groups
+        // by their best key (lane g holds group g's), keep the best
+        // topk_groups -- ties to the lower group, i.e. the lower lane -- and
+        // drop every expert outside them
+        const int32_t gsize = E / n_groups;
+        int gid[NSLOT];
+#pragma unroll
+        for (int i = 0; i < NSLOT; ++i)
+            gid[i] = (int)(slot_id<VEC>(i, lane) / (uint32_t)gsize);
+        uint32_t my_gkey = 0u;
+        for (int g = 0; g < n_groups; ++g) {
+            uint32_t v = 0u;
+#pragma unroll
+            for (int i = 0; i < NSLOT; ++i)
+                v = gid[i] == g ? max(v, key[i]) : v;
+            const uint32_t best = wave_max_u32(v);
+            my_gkey = lane == g ? best : my_gkey;
+        }
+        uint64_t chosen = 0;
+        for (int m = 0; m < topk_groups; ++m) {
+            const uint32_t best = wave_max_u32(my_gkey);
+            const uint64_t holders = ballot64(my_gkey == best && lane < n_groups);
+            const int g = __ffsll((unsigned long long)holders) - 1;
+            chosen |= 1ull << g;
+            my_gkey = lane == g ? 0u : my_gkey;
+        }
+#pragma unroll
+        for (int i = 0; i < NSLOT; ++i)
+            key[i] = ((chosen >> gid[i]) & 1ull) ? key[i] : 0u;
     }
 
     // the lane's two best entries; ascending i is ascending id, so strict
@@ -178,35 +216,36 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
 
 template <int NSLOT, int VEC>
 hipError_t launch_slots(const float *logits, const float *bias, int64_t T, int32_t E, int32_t k,
-                        bool normalize, int32_t *topk_idx, float *topk_w, hipStream_t stream)
+                        int32_t n_groups, int32_t topk_groups, bool normalize, int32_t *topk_idx,
+                        float *topk_w, hipStream_t stream)
 {
     const dim3 grid((unsigned)((T + kTokensPerBlock - 1) / kTokensPerBlock));
     if (normalize)
         hipLaunchKernelGGL((route_topk_kernel<NSLOT, VEC, true>), grid, dim3(kRouteThreads), 0,
-                           stream, logits, bias, T, E, k, topk_idx, topk_w);
+                           stream, logits, bias, T, E, k, n_groups, topk_groups, topk_idx, topk_w);
     else
         hipLaunchKernelGGL((route_topk_kernel<NSLOT, VEC, false>), grid, dim3(kRouteThreads), 0,
-                           stream, logits, bias, T, E, k, topk_idx, topk_w);
+                           stream, logits, bias, T, E, k, n_groups, topk_groups, topk_idx, topk_w);
     return hipGetLastError();
 }
 
 }  // namespace
 
 hipError_t launch_route_topk(const float *logits, const float *bias, int64_t T, int32_t E,
-                             int32_t k, bool normalize, int32_t *topk_idx, float *topk_w,
-                             hipStream_t stream)
+                             int32_t k, int32_t n_groups, int32_t topk_groups, bool normalize,
+                             int32_t *topk_idx, float *topk_w, hipStream_t stream)
 {
     const bool vec4 = E % 4 == 0 && (uintptr_t)logits % 16 == 0 && (uintptr_t)bias % 16 == 0;
     if (vec4) {
         switch ((E + 4 * kWave - 1) / (4 * kWave)) {
         case 1:
-            return launch_slots<4, 4>(logits, bias, T, E, k, normalize, topk_idx, topk_w, stream);
+            return launch_slots<4, 4>(logits, bias, T, E, k, n_groups, topk_groups, normalize, topk_idx, topk_w, stream);
         case 2:
-            return launch_slots<8, 4>(logits, bias, T, E, k, normalize, topk_idx, topk_w, stream);
+            return launch_slots<8, 4>(logits, bias, T, E, k, n_groups, topk_groups, normalize, topk_idx, topk_w, stream);
         case 3:
-            return launch_slots<12, 4>(logits, bias, T, E, k, normalize, topk_idx, topk_w, stream);
+            return launch_slots<12, 4>(logits, bias, T, E, k, n_groups, topk_groups, normalize, topk_idx, topk_w, stream);
         case 4:
-            return launch_slots<16, 4>(logits, bias, T, E, k, normalize, topk_idx, topk_w, stream);
+            return launch_slots<16, 4>(logits, bias, T, E, k, n_groups, topk_groups, normalize, topk_idx, topk_w, stream);
         default:
             return hipErrorInvalidValue;
         }
@@ -214,7 +253,7 @@ hipError_t launch_route_topk(const float *logits, const float *bias, int64_t T, 
     switch ((E + kWave - 1) / kWave) {
 #define MOE_ROUTE_CASE(n) \
     case n:               \
-        return launch_slots<n, 1>(logits, bias, T, E, k, normalize, topk_idx, topk_w, stream);
+        return launch_slots<n, 1>(logits, bias, T, E, k, n_groups, topk_groups, normalize, topk_idx, topk_w, stream);
         MOE_ROUTE_CASE(1)
         MOE_ROUTE_CASE(2)
         MOE_ROUTE_CASE(3)

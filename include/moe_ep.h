@@ -88,6 +88,36 @@ moe_status_t moe_route_topk(const float *logits, const float *bias,
                             int32_t *topk_idx, float *topk_w, void *stream);
 
 /*
+ * moe_route_topk_grouped -- group-limited routing: each token may use at
+ * most topk_groups of n_groups contiguous expert groups (destination groups
+ * such as nodes), then picks its k experts inside them.
+ *
+ * Defined by: ai-from-scratch "19. All-to-all", "DeepSeek's numbers" (each
+ * token limited to at most 4 nodes, so the slow hop stays bounded) and the
+ * closing section (node-limited routing as an architectural constraint);
+ * zenaique Q&A "moe-hide-alltoall-techniques" (node-limited routing caps
+ * cross-node traffic). The pages do not define a group's score; this call
+ * ranks groups by their best selection score s[e] (as moe_route_topk orders
+ * experts, so ties go to the lower group), keeps the best topk_groups, and
+ * selects the k best experts among them. Gate weights are computed exactly
+ * as in moe_route_topk, from the selected experts' unbiased logits.
+ *
+ * Arguments: as moe_route_topk, plus
+ *   n_groups    groups of E / n_groups experts each; E % n_groups == 0,
+ *               1 <= n_groups <= 64.
+ *   topk_groups 1 <= topk_groups <= n_groups and
+ *               k <= topk_groups * (E / n_groups).
+ *   topk_groups == n_groups is plain moe_route_topk.
+ * Errors: MOE_ERR_INVALID_ARG for bad pointers or group sizes;
+ *   MOE_ERR_UNSUPPORTED outside the limits (n_groups > 64 included).
+ */
+moe_status_t moe_route_topk_grouped(const float *logits, const float *bias,
+                                    int64_t T, int32_t E, int32_t k,
+                                    int32_t n_groups, int32_t topk_groups,
+                                    uint32_t flags, int32_t *topk_idx,
+                                    float *topk_w, void *stream);
+
+/*
  * moe_layout_workspace_size -- bytes of device workspace that
  * moe_dispatch_layout needs for these sizes (written to *bytes). The
  * workspace needs no initialisation: the layout call clears what it uses,

@@ -62,6 +62,21 @@ def test_route_validation(moe):
     assert lib.moe_route_topk(None, None, 0, 8, 2, 1, None, None, None) == moe.MOE_OK
 
 
+def test_grouped_route_validation(moe):
+    lib = moe.lib
+    g = lambda E=64, k=4, G=8, M=2, T=4, flags=1, lg=FAKE: lib.moe_route_topk_grouped(
+        lg, None, T, E, k, G, M, flags, FAKE, FAKE, None)
+    assert g(G=6) == moe.MOE_ERR_INVALID_ARG          # E % n_groups != 0
+    assert g(G=0) == moe.MOE_ERR_INVALID_ARG
+    assert g(M=0) == moe.MOE_ERR_INVALID_ARG
+    assert g(M=9) == moe.MOE_ERR_INVALID_ARG          # topk_groups > n_groups
+    assert g(k=17, M=2) == moe.MOE_ERR_INVALID_ARG    # k > 2 groups x 8 experts
+    assert g(E=256, G=128, M=4, k=4) == moe.MOE_ERR_UNSUPPORTED
+    assert g(lg=None) == moe.MOE_ERR_INVALID_ARG
+    assert g(flags=4) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_topk_grouped(None, None, 0, 64, 4, 8, 2, 1, None, None, None) == moe.MOE_OK
+
+
 def test_workspace_size(moe):
     # one E-wide int32 histogram per tile: tiles of 2048 assignments, at most
     # 128 of them; up to 4096 assignments (E <= 512) need no workspace

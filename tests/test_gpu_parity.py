@@ -400,3 +400,33 @@ def test_route_misaligned_rows(moe, E):
     o_idx, o_w = oracle.route_topk(logits, bias, k)
     np.testing.assert_array_equal(idx.cpu().numpy(), o_idx)
     assert np.all(np.abs(wt.cpu().numpy() - o_w) <= weight_tolerance(logits, o_idx, o_w, k))
+
+
+GROUPED = [
+    # T, E, k, n_groups, topk_groups, bias
+    (32768, 512, 10, 8, 4, None),      # fine-grained shape, 8 groups of 64, at most 4
+    (4096, 384, 8, 64, 4, "uniform"),  # one group per destination of 6 experts
+    (999, 256, 8, 32, 8, "uniform"),
+    (500, 100, 7, 4, 2, None),         # E % 4 == 0 but tiny groups of 25
+    (333, 70, 6, 7, 2, "uniform"),     # 4-byte route path
+    (200, 64, 4, 64, 4, None),         # one expert per group: plain top-k
+    (300, 64, 6, 8, 8, None),          # every group allowed: plain top-k
+]
+
+
+@pytest.mark.parametrize("case", GROUPED, ids=[str(c) for c in GROUPED])
+def test_route_topk_grouped(moe, case):
+    T, E, k, G, M, b = case
+    r = np.random.default_rng(T + E + G)
+    logits = r.standard_normal((T, E), dtype=np.float32)
+    logits[::13, 3] = np.nan
+    logits[::7, E // 2] = logits[::7, E // 2 + 1]            # exact ties
+    bias = r.uniform(-0.1, 0.1, E).astype(np.float32) if b else None
+    say(f"route_topk_grouped T={T} E={E} k={k} groups={G} topk_groups={M}")
+    idx, wt = moe.moe_route_topk_grouped(up(logits), None if bias is None else up(bias), k, G, M)
+    torch.cuda.synchronize()
+    o_idx, o_w = oracle.route_topk_grouped(logits, bias, k, G, M)
+    np.testing.assert_array_equal(idx.cpu().numpy(), o_idx)
+    finite = np.isfinite(o_w).all(axis=1)
+    tol = weight_tolerance(logits, o_idx, o_w, k)
+    assert np.all(np.abs(wt.cpu().numpy() - o_w)[finite] <= tol[finite])
