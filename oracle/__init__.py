@@ -54,12 +54,16 @@ def _load():
         lib.oracle_route_topk_grouped.argtypes = [P, P, i64, i32, i32, i32, i32, i32, P, P]
         lib.oracle_dispatch_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P]
         lib.oracle_dispatch_permute.argtypes = [P, P, i64, i32, i32, P, i64]
+        lib.oracle_recv_regroup_layout.argtypes = [P, i32, i32, P, P, P]
+        lib.oracle_scatter_rows.argtypes = [P, P, i64, i32, P, i64]
+        lib.oracle_gather_rows.argtypes = [P, i64, P, i64, i32, P]
         lib.oracle_combine_reduce.argtypes = [P, i64, P, P, P, P, i64, i32, i32, P, i64, P]
         lib.oracle_bf16_round.argtypes = [ctypes.c_double]
         lib.oracle_bf16_round.restype = ctypes.c_uint16
         lib.oracle_bf16_round_array.argtypes = [P, i64, P]
         for f in ("oracle_route_topk", "oracle_route_topk_grouped", "oracle_dispatch_layout",
-                  "oracle_dispatch_permute", "oracle_combine_reduce"):
+                  "oracle_dispatch_permute", "oracle_combine_reduce", "oracle_recv_regroup_layout",
+                  "oracle_scatter_rows", "oracle_gather_rows"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -143,6 +147,45 @@ def dispatch_permute(x: np.ndarray, pos: np.ndarray, send_rows: int,
     if rc != 0:
         raise ValueError("oracle_dispatch_permute: position outside the send buffer")
     return send
+
+
+def recv_regroup_layout(cnt: np.ndarray) -> dict:
+    """Expert-major layout of a source-major receive buffer with cnt[s][l]
+    rows of local expert l from source s; see oracle_recv_regroup_layout."""
+    cnt = _c(cnt, np.int32)
+    S, El = cnt.shape
+    N = int(cnt.sum())
+    out = {"local_expert_offsets": np.empty(El + 1, np.int32),
+           "source_offsets": np.empty(S + 1, np.int32),
+           "recv_pos": np.empty(N, np.int32)}
+    rc = _load().oracle_recv_regroup_layout(_ptr(cnt), S, El, _ptr(out["local_expert_offsets"]),
+                                            _ptr(out["source_offsets"]), _ptr(out["recv_pos"]))
+    if rc != 0:
+        raise ValueError("oracle_recv_regroup_layout rejected its arguments")
+    return out
+
+
+def scatter_rows(src: np.ndarray, row_map: np.ndarray, dst_rows: int, fill: int = 0) -> np.ndarray:
+    """dst[row_map[i]] = src[i]; rows no entry points at hold `fill`."""
+    src = _c(src, np.uint16)
+    row_map = _c(row_map, np.int32)
+    n, H = src.shape
+    dst = np.full((dst_rows, H), fill, np.uint16)
+    if _load().oracle_scatter_rows(_ptr(src), _ptr(row_map), n, H, _ptr(dst), dst_rows) != 0:
+        raise ValueError("oracle_scatter_rows: target row out of range")
+    return dst
+
+
+def gather_rows(src: np.ndarray, row_map: np.ndarray) -> np.ndarray:
+    """dst[i] = src[row_map[i]]."""
+    src = _c(src, np.uint16)
+    row_map = _c(row_map, np.int32)
+    H = src.shape[1]
+    dst = np.empty((row_map.shape[0], H), np.uint16)
+    if _load().oracle_gather_rows(_ptr(src), src.shape[0], _ptr(row_map), row_map.shape[0], H,
+                                  _ptr(dst)) != 0:
+        raise ValueError("oracle_gather_rows: source row out of range")
+    return dst
 
 
 def combine_reduce(y: np.ndarray, pos: np.ndarray, w: np.ndarray,

@@ -369,6 +369,99 @@ int oracle_dispatch_layout(const int32_t *topk_idx, int64_t T, int32_t E,
 }
 
 /* ------------------------------------------------------------------ */
+/* receive side: regroup source-major segments into expert-major rows  */
+/* ------------------------------------------------------------------ */
+
+/*
+ * A destination receives, from each of S sources in source order, one
+ * contiguous segment holding that source's rows for the destination's E_l
+ * local experts, grouped by local expert (cnt[s][l] rows of expert l from
+ * source s; the counts exchange delivers cnt). The expert computation wants
+ * each local expert's rows together, so the rows are regrouped expert-major,
+ * sources in order inside each expert:
+ *   local_expert_offsets[l] = rows of experts < l over all sources
+ *   source_offsets[s]       = rows of sources < s over all experts
+ *   received row i (source s, expert l, j-th of that block) goes to
+ *   recv_pos[i] = local_expert_offsets[l] + sum_{s' < s} cnt[s'][l] + j.
+ * N = source_offsets[S] = local_expert_offsets[E_l]. Returns 0, or -1 on
+ * bad sizes or negative counts.
+ *
+ * Source: aicassindra "gpu_moe_all_to_all", "Two collectives per layer"
+ * (counts precede the payload so that receivers can size buffers; outputs
+ * return along the inverse permutation) and "Bucketing" (one contiguous
+ * message per peer); "MoE All-to-All Dispatch and Ragged Routing", "Why MoE
+ * Token Dispatch is All-to-All" (a GPU holds 6 of 384 experts) and "Fixed
+ * Capacity vs. Ragged Routing" (variable-length exchange pooled over the
+ * local experts).
+ */
+int oracle_recv_regroup_layout(const int32_t *cnt, int32_t S, int32_t E_l,
+                               int32_t *local_expert_offsets,
+                               int32_t *source_offsets, int32_t *recv_pos)
+{
+    if (S <= 0 || E_l <= 0)
+        return -1;
+    for (int32_t i = 0; i < S * E_l; ++i)
+        if (cnt[i] < 0)
+            return -1;
+    local_expert_offsets[0] = 0;
+    for (int32_t l = 0; l < E_l; ++l) {
+        int32_t col = 0;
+        for (int32_t src = 0; src < S; ++src)
+            col += cnt[src * E_l + l];
+        local_expert_offsets[l + 1] = local_expert_offsets[l] + col;
+    }
+    source_offsets[0] = 0;
+    for (int32_t src = 0; src < S; ++src) {
+        int32_t rowsum = 0;
+        for (int32_t l = 0; l < E_l; ++l)
+            rowsum += cnt[src * E_l + l];
+        source_offsets[src + 1] = source_offsets[src] + rowsum;
+    }
+    int64_t i = 0;
+    for (int32_t src = 0; src < S; ++src) {
+        for (int32_t l = 0; l < E_l; ++l) {
+            int32_t before = 0;   /* rows of expert l from earlier sources */
+            for (int32_t s2 = 0; s2 < src; ++s2)
+                before += cnt[s2 * E_l + l];
+            for (int32_t j = 0; j < cnt[src * E_l + l]; ++j)
+                recv_pos[i++] = local_expert_offsets[l] + before + j;
+        }
+    }
+    return 0;
+}
+
+/*
+ * Move rows by a map: dst[map[i]][:] = src[i][:] for i < n (bit copies).
+ * The regroup applies recv_pos this way; the return path applies it the
+ * other way round (oracle_gather_rows). Returns -1 when a target falls
+ * outside [0, dst_rows).
+ */
+int oracle_scatter_rows(const uint16_t *src, const int32_t *map, int64_t n, int32_t H,
+                        uint16_t *dst, int64_t dst_rows)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        if (map[i] < 0 || map[i] >= dst_rows)
+            return -1;
+        for (int32_t h = 0; h < H; ++h)
+            dst[(int64_t)map[i] * H + h] = src[i * H + h];
+    }
+    return 0;
+}
+
+/* dst[i][:] = src[map[i]][:] for i < n; -1 when a source row is out of range. */
+int oracle_gather_rows(const uint16_t *src, int64_t src_rows, const int32_t *map, int64_t n,
+                       int32_t H, uint16_t *dst)
+{
+    for (int64_t i = 0; i < n; ++i) {
+        if (map[i] < 0 || map[i] >= src_rows)
+            return -1;
+        for (int32_t h = 0; h < H; ++h)
+            dst[i * H + h] = src[(int64_t)map[i] * H + h];
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
 /* dispatch permute: pack each kept replica into its send row          */
 /* ------------------------------------------------------------------ */
 

@@ -13,7 +13,8 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
-PIN_TESTS = ["tests/test_oracle_route.py", "tests/test_oracle_layout.py", "tests/test_oracle_combine.py"]
+PIN_TESTS = ["tests/test_oracle_route.py", "tests/test_oracle_layout.py", "tests/test_oracle_combine.py",
+             "tests/test_oracle_regroup.py"]
 
 MUTATIONS = {
     "tie_break_to_higher_id": ("    return ia < ib;\n", "    return ia > ib;\n"),
@@ -38,6 +39,9 @@ MUTATIONS = {
     "group_score_from_worst_member": ("                if (ranks_above(s[e], e, s[best], best))\n                    best = e;\n            gbest[g] = best;",
                                       "                if (ranks_above(s[best], best, s[e], e))\n                    best = e;\n            gbest[g] = best;"),
     "group_mask_ignored": ("            taken[e] = !gsel[e / gsize];", "            taken[e] = 0;"),
+    "regroup_counts_earlier_experts": ("                before += cnt[s2 * E_l + l];", "                before += cnt[src * E_l + s2 % E_l];"),
+    "regroup_expert_base_off_by_one": ("                recv_pos[i++] = local_expert_offsets[l] + before + j;",
+                                       "                recv_pos[i++] = local_expert_offsets[l] + before + j + (l > 0);"),
     "bf16_ties_away_from_zero": ("double r = nearbyint(a / q) * q;", "double r = round(a / q) * q;"),
     "bf16_no_subnormal_spacing": ("if (e < -126)\n        e = -126;", "if (e < -140)\n        e = -140;"),
 }
