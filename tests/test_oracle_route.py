@@ -143,6 +143,8 @@ def test_bias_is_selection_only(orc):
 
 def test_golden_route(orc):
     for case in _golden():
+        if "logits" not in case:
+            continue
         logits = np.array(case["logits"], np.float32)
         bias = None if case["bias"] is None else np.array(case["bias"], np.float32)
         idx, w = orc.route_topk(logits, bias, case["k"])
