@@ -20,6 +20,10 @@ for kept rows only:
 with N kept rows and T_read tokens that have at least one kept replica (both
 read from the path's own outputs after the timed region).
 
+After the path, the receive-side regroup is timed on the same buffers (the
+send buffer read as R source segments) and reported under "next_rows"; it
+is not part of `value`.
+
 The CPU-baseline leg times the plain C oracle on the same host arrays.
 """
 
@@ -61,6 +65,8 @@ def parse():
     p.add_argument("--workload", default="fine_grained",
                    help="one of " + ", ".join(w.name for w in synthetic.WORKLOADS.values()))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-regroup", action="store_true",
+                   help="skip the receive-side regroup measurement (reported under next_rows)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
                    help="rough CPU time budget of the oracle baseline")
     p.add_argument("--route-groups", default=None, metavar="G,M",
@@ -104,6 +110,76 @@ def stored_traffic(kernel, workload):
     if rec.get("source_sha256_16") != source_hash(KERNEL_SOURCES[kernel]):
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def bench_regroup(moe, torch, lay, send, S, El, H, rows, stream, warmup, steps):
+    """Receive-side regroup on this GPU's share: the send buffer read as a
+    receive buffer of S source segments with El local experts each (counts =
+    the layout's expert counts), regrouped expert-major and back. Per-call
+    event pairs; algorithmic bytes per call:
+      layout   S*El*4 + (El + S + 2)*4 + N*4
+      regroup  N*H*2 read + N*H*2 write + N*4
+      ungroup  the same."""
+    dev = send.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    cnt = lay["expert_counts"].view(S, El)
+    L = {"local_expert_offsets": torch.empty(El + 1, **i32), "source_offsets": torch.empty(S + 1, **i32),
+         "recv_pos": torch.empty(rows, **i32)}
+    ws = torch.empty(moe.moe_recv_regroup_workspace_size(S, El), dtype=torch.uint8, device=dev)
+    grouped = torch.empty_like(send)
+    back = torch.empty_like(send)
+    n_rows = L["source_offsets"][S:]
+    sp = stream.cuda_stream
+    lib, P = moe.lib, (lambda t: t.data_ptr())
+
+    def check(name, rc):
+        if rc != moe.MOE_OK:
+            raise RuntimeError(f"{name}: {moe.moe_status_string(rc)}")
+
+    calls = [
+        ("layout", lambda: check("regroup layout", lib.moe_recv_regroup_layout(
+            P(cnt), S, El, P(L["local_expert_offsets"]), P(L["source_offsets"]), P(L["recv_pos"]),
+            rows, P(ws), ws.numel(), sp))),
+        ("regroup", lambda: check("regroup", lib.moe_recv_regroup(
+            P(send), P(L["recv_pos"]), P(n_rows), rows, H, P(grouped), sp))),
+        ("ungroup", lambda: check("ungroup", lib.moe_recv_ungroup(
+            P(grouped), P(L["recv_pos"]), P(n_rows), rows, H, P(back), sp))),
+    ]
+    for _ in range(warmup):
+        for _, fn in calls:
+            fn()
+    torch.cuda.synchronize()
+    beg, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    beg.record(stream)
+    for _ in range(steps):
+        for _, fn in calls:
+            fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    us_pass = beg.elapsed_time(end) / steps * 1e3
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(steps)]
+    for s in range(steps):
+        for i, (_, fn) in enumerate(calls):
+            ev[s][i].record(stream)
+            fn()
+        ev[s][len(calls)].record(stream)
+    torch.cuda.synchronize()
+    us = {name: statistics.mean(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) * 1e3
+          for i, (name, _) in enumerate(calls)}
+    N = int(L["source_offsets"][S].item())
+    if not torch.equal(back[:N].view(torch.int16), send[:N].view(torch.int16)):
+        raise RuntimeError("regroup round trip did not return the receive buffer")
+    nb = {"layout": S * El * 4 + (El + S + 2) * 4 + N * 4,
+          "regroup": 2 * N * H * 2 + N * 4, "ungroup": 2 * N * H * 2 + N * 4}
+    gbps = {n: nb[n] / (us[n] * 1e-6) / 1e9 for n in nb}
+    out = {"sources": S, "local_experts": El, "rows": N, "us_per_pass": round(us_pass, 2),
+           "per_call_us": {n: round(v, 2) for n, v in us.items()},
+           "per_call_GBps": {n: round(v, 1) for n, v in gbps.items()},
+           "roofline": {"bound": "hbm", "kernel": "regroup_rows_kernel", "achieved": round(gbps["regroup"], 1),
+                        "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                        "frac": round(gbps["regroup"] / HBM_PEAK_GBPS, 4), "algorithmic_bytes": nb["regroup"]}}
+    log("regroup", out)
+    return out
 
 
 def cpu_baseline(w, d, budget_s):
@@ -247,6 +323,9 @@ def main():
                 "kernel": kname, "algorithmic_bytes": nbytes[dominant],
                 "avg_launch_us": round(per_call_ms[dominant] * 1e3, 2)}
 
+    regroup = None if args.no_regroup or R < 2 else bench_regroup(
+        moe, torch, lay, send, R, E // R, H, send_rows, stream, args.warmup, args.steps)
+
     copy_probe = None
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 2
@@ -290,6 +369,8 @@ def main():
         "per_call_GBps": {n: round(nbytes[n] / (per_call_ms[n] * 1e-3) / 1e9, 1) for n in nbytes},
         "roofline": roofline,
     }
+    if regroup:
+        result["next_rows"] = {"recv_regroup": regroup}
     if copy_probe:
         result["copy_probe"] = copy_probe
 

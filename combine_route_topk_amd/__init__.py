@@ -29,7 +29,8 @@ MOE_ROUTE_NORMALIZE = 1
 MOE_COMBINE_OUT_FP32 = 1
 
 EXPORTS = ("moe_route_topk", "moe_route_topk_grouped", "moe_layout_workspace_size", "moe_dispatch_layout",
-           "moe_dispatch_permute", "moe_combine_reduce", "moe_status_string")
+           "moe_dispatch_permute", "moe_combine_reduce", "moe_recv_regroup_workspace_size",
+           "moe_recv_regroup_layout", "moe_recv_regroup", "moe_recv_ungroup", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -52,6 +53,10 @@ def _load_library() -> ctypes.CDLL:
                                         ctypes.c_size_t, P]
     lib.moe_dispatch_permute.argtypes = [P, P, i64, i32, i32, P, i64, P]
     lib.moe_combine_reduce.argtypes = [P, i64, P, P, P, P, i64, i32, i32, u32, P, P]
+    lib.moe_recv_regroup_workspace_size.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_recv_regroup_layout.argtypes = [P, i32, i32, P, P, P, i64, P, ctypes.c_size_t, P]
+    lib.moe_recv_regroup.argtypes = [P, P, P, i64, i32, P, P]
+    lib.moe_recv_ungroup.argtypes = [P, P, P, i64, i32, P, P]
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     for name in EXPORTS[:-1]:
@@ -205,4 +210,55 @@ def moe_combine_reduce(y: torch.Tensor, pos: torch.Tensor, topk_w: torch.Tensor,
         _ptr(topk_w, _F32, "topk_w"), _ptr(shared, _BF16, "shared", 2),
         _ptr(residual, _BF16, "residual", 2), T, H, k,
         MOE_COMBINE_OUT_FP32 if out_fp32 else 0, _ptr(out, want, "out"), _stream(stream)))
+    return out
+
+
+def moe_recv_regroup_workspace_size(S: int, E_l: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_recv_regroup_workspace_size", lib.moe_recv_regroup_workspace_size(S, E_l, ctypes.byref(n)))
+    return n.value
+
+
+def moe_recv_regroup_layout(recv_counts: torch.Tensor, max_rows: int, out: Optional[dict] = None,
+                            workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Expert-major layout of a source-major receive buffer (see
+    moe_recv_regroup_layout). Returns int32 GPU tensors local_expert_offsets
+    [E_l+1], source_offsets [S+1] and recv_pos [max_rows]."""
+    S, El = recv_counts.shape
+    dev = recv_counts.device
+    o = dict(out or {})
+    for name, n in (("local_expert_offsets", El + 1), ("source_offsets", S + 1), ("recv_pos", max_rows)):
+        if o.get(name) is None:
+            o[name] = torch.empty(n, dtype=torch.int32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(moe_recv_regroup_workspace_size(S, El), dtype=torch.uint8, device=dev)
+    _check("moe_recv_regroup_layout", lib.moe_recv_regroup_layout(
+        _ptr(recv_counts, _I32, "recv_counts", 2), S, El,
+        _ptr(o["local_expert_offsets"], _I32, "local_expert_offsets"),
+        _ptr(o["source_offsets"], _I32, "source_offsets"), _ptr(o["recv_pos"], _I32, "recv_pos"),
+        max_rows, _ptr(workspace, (torch.uint8,), "workspace"), workspace.numel(), _stream(stream)))
+    return o
+
+
+def moe_recv_regroup(recv: torch.Tensor, recv_pos: torch.Tensor, n_rows: torch.Tensor,
+                     grouped: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """grouped[recv_pos[i]] = recv[i] for i < n_rows (device scalar)."""
+    rows, H = recv.shape
+    if grouped is None:
+        grouped = torch.empty_like(recv)
+    _check("moe_recv_regroup", lib.moe_recv_regroup(
+        _ptr(recv, _BF16, "recv", 2), _ptr(recv_pos, _I32, "recv_pos"), _ptr(n_rows, _I32, "n_rows"),
+        rows, H, _ptr(grouped, _BF16, "grouped"), _stream(stream)))
+    return grouped
+
+
+def moe_recv_ungroup(grouped: torch.Tensor, recv_pos: torch.Tensor, n_rows: torch.Tensor,
+                     out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """out[i] = grouped[recv_pos[i]] for i < n_rows (device scalar)."""
+    rows, H = grouped.shape
+    if out is None:
+        out = torch.empty_like(grouped)
+    _check("moe_recv_ungroup", lib.moe_recv_ungroup(
+        _ptr(grouped, _BF16, "grouped", 2), _ptr(recv_pos, _I32, "recv_pos"), _ptr(n_rows, _I32, "n_rows"),
+        rows, H, _ptr(out, _BF16, "out"), _stream(stream)))
     return out

@@ -11,6 +11,8 @@ constexpr int32_t kMaxE = 1024;
 constexpr int32_t kMaxK = 32;
 constexpr int32_t kMaxH = 65536;
 constexpr int32_t kMaxGroups = 64;
+constexpr int32_t kMaxRegroupSide = 1024;
+constexpr int32_t kMaxRegroupBlocks = 4096;
 constexpr int64_t kMaxAssignments = (int64_t)1 << 31;
 
 bool aligned(const void *p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -54,6 +56,33 @@ moe_status_t check_layout_sizes(int64_t T, int32_t E, int32_t k, int32_t R)
 }
 
 moe_status_t from_hip(hipError_t err) { return err == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
+
+moe_status_t check_regroup_sizes(int32_t S, int32_t El)
+{
+    if (S < 1 || El < 1)
+        return MOE_ERR_INVALID_ARG;
+    if (S > kMaxRegroupSide || El > kMaxRegroupSide || (int64_t)S * El > kMaxRegroupBlocks)
+        return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+moe_status_t regroup_rows(const uint16_t *src, const int32_t *map, const int32_t *n_rows,
+                          int64_t max_rows, int32_t H, bool gather, uint16_t *dst, void *stream)
+{
+    if (max_rows < 0 || max_rows >= kMaxAssignments)
+        return max_rows < 0 ? MOE_ERR_INVALID_ARG : MOE_ERR_UNSUPPORTED;
+    moe_status_t s = check_hidden(H);
+    if (s != MOE_OK)
+        return s;
+    if (max_rows == 0)
+        return MOE_OK;
+    if (!src || !map || !n_rows || !dst)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(src, 16) || !aligned(dst, 16) || !aligned(map, 4) || !aligned(n_rows, 4))
+        return MOE_ERR_INVALID_ARG;
+    return from_hip(moe::launch_regroup_rows(src, map, n_rows, max_rows, H, gather, dst,
+                                             static_cast<hipStream_t>(stream)));
+}
 
 }  // namespace
 
@@ -191,6 +220,57 @@ moe_status_t moe_combine_reduce(const uint16_t *y, int64_t y_rows, const int32_t
     return from_hip(moe::launch_combine_reduce(y, y_rows, pos, topk_w, shared, residual, T, H, k,
                                                (flags & MOE_COMBINE_OUT_FP32) != 0, out,
                                                static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_recv_regroup_workspace_size(int32_t S, int32_t El, size_t *bytes)
+{
+    if (!bytes)
+        return MOE_ERR_INVALID_ARG;
+    moe_status_t s = check_regroup_sizes(S, El);
+    if (s != MOE_OK)
+        return s;
+    *bytes = moe::regroup_workspace_bytes(S, El);
+    return MOE_OK;
+}
+
+moe_status_t moe_recv_regroup_layout(const int32_t *recv_counts, int32_t S, int32_t El,
+                                     int32_t *local_expert_offsets, int32_t *source_offsets,
+                                     int32_t *recv_pos, int64_t max_rows, void *workspace,
+                                     size_t workspace_bytes, void *stream)
+{
+    moe_status_t s = check_regroup_sizes(S, El);
+    if (s != MOE_OK)
+        return s;
+    if (max_rows < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (max_rows >= kMaxAssignments)
+        return MOE_ERR_UNSUPPORTED;
+    if (!recv_counts || !local_expert_offsets || !source_offsets || (max_rows > 0 && !recv_pos))
+        return MOE_ERR_INVALID_ARG;
+    const void *ptrs[] = {recv_counts, local_expert_offsets, source_offsets, recv_pos};
+    for (const void *p : ptrs)
+        if (!aligned(p, 4))
+            return MOE_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < moe::regroup_workspace_bytes(S, El) ||
+        !aligned(workspace, 16))
+        return MOE_ERR_WORKSPACE;
+    return from_hip(moe::launch_recv_regroup_layout(
+        recv_counts, S, El, local_expert_offsets, source_offsets, recv_pos, max_rows,
+        static_cast<int32_t *>(workspace), static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_recv_regroup(const uint16_t *recv, const int32_t *recv_pos,
+                              const int32_t *n_rows, int64_t max_rows, int32_t H,
+                              uint16_t *grouped, void *stream)
+{
+    return regroup_rows(recv, recv_pos, n_rows, max_rows, H, false, grouped, stream);
+}
+
+moe_status_t moe_recv_ungroup(const uint16_t *grouped, const int32_t *recv_pos,
+                              const int32_t *n_rows, int64_t max_rows, int32_t H, uint16_t *out,
+                              void *stream)
+{
+    return regroup_rows(grouped, recv_pos, n_rows, max_rows, H, true, out, stream);
 }
 
 const char *moe_status_string(moe_status_t status)

@@ -53,4 +53,14 @@ hipError_t launch_combine_reduce(const uint16_t *y, int64_t y_rows, const int32_
                                  const uint16_t *residual, int64_t T, int32_t H, int32_t k,
                                  bool out_fp32, void *out, hipStream_t stream);
 
+// Receive-side regroup (regroup.hip).
+size_t regroup_workspace_bytes(int32_t S, int32_t El);
+hipError_t launch_recv_regroup_layout(const int32_t *recv_counts, int32_t S, int32_t El,
+                                      int32_t *local_expert_offsets, int32_t *source_offsets,
+                                      int32_t *recv_pos, int64_t max_rows, int32_t *workspace,
+                                      hipStream_t stream);
+hipError_t launch_regroup_rows(const uint16_t *src, const int32_t *map, const int32_t *n_rows,
+                               int64_t max_rows, int32_t H, bool gather, uint16_t *dst,
+                               hipStream_t stream);
+
 }  // namespace moe

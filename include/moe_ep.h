@@ -244,6 +244,73 @@ moe_status_t moe_combine_reduce(const uint16_t *y, int64_t y_rows,
                                 int32_t H, int32_t k, uint32_t flags,
                                 void *out, void *stream);
 
+/*
+ * Receive side: regroup a destination's receive buffer into expert-major
+ * rows for the expert computation, and back for the return path.
+ *
+ * Defined by: aicassindra "gpu_moe_all_to_all", "Two collectives per layer"
+ * (per-destination counts arrive before the payload so that the receiver
+ * can size and place it; outputs return along the inverse permutation) and
+ * "Bucketing" (one contiguous message per peer); "MoE All-to-All Dispatch
+ * and Ragged Routing", "Why MoE Token Dispatch is All-to-All" (a GPU holds a
+ * few of the experts) and "Fixed Capacity vs. Ragged Routing" (variable-
+ * length exchange, the receiver pooling its local experts).
+ *
+ * The receive buffer is the concatenation, in source order, of one segment
+ * per source s; each segment holds recv_counts[s][l] rows of local expert l
+ * (l ascending), i.e. rows dest_offsets[r]..dest_offsets[r+1] of that
+ * source's send buffer and expert_counts[r*E_l + l] of its counts. With
+ * N = sum of recv_counts:
+ *   local_expert_offsets[l] = rows of local experts < l     (E_l + 1 entries)
+ *   source_offsets[s]       = rows of sources < s           (S + 1 entries)
+ *   recv_pos[i]             = expert-major row of received row i: the block
+ *                             (s, l) holding row i starts at
+ *                             local_expert_offsets[l] + sum_{s' < s} recv_counts[s'][l]
+ * so each local expert's rows are contiguous, sources in order within it.
+ * N stays on the device: local_expert_offsets[E_l] == source_offsets[S].
+ */
+
+/* Workspace bytes for moe_recv_regroup_layout (written to *bytes). */
+moe_status_t moe_recv_regroup_workspace_size(int32_t S, int32_t E_l, size_t *bytes);
+
+/*
+ * moe_recv_regroup_layout -- the offsets and recv_pos above.
+ *   recv_counts [S][E_l] int32 (device; negative entries count as 0).
+ *   recv_pos    [max_rows] int32; entries past N are not written, and rows
+ *               past max_rows are not placed (a broken precondition when
+ *               N > max_rows).
+ *   workspace   moe_recv_regroup_workspace_size() bytes, 16-byte aligned;
+ *               contents on entry do not matter.
+ * Limits: 1 <= S, E_l <= 1024 and S * E_l <= 4096; max_rows < 2^31.
+ * Device-side precondition: the counts total less than 2^31.
+ * Errors: MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE.
+ */
+moe_status_t moe_recv_regroup_layout(const int32_t *recv_counts, int32_t S, int32_t E_l,
+                                     int32_t *local_expert_offsets,
+                                     int32_t *source_offsets, int32_t *recv_pos,
+                                     int64_t max_rows, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
+/*
+ * moe_recv_regroup -- grouped[recv_pos[i]][:] = recv[i][:] for i < N (bit
+ * copies of bf16 rows). n_rows points at N on the device (for example
+ * source_offsets + S); max_rows bounds the grid and both buffers' rows.
+ * recv and grouped are [max_rows][H] bf16, 16-byte aligned, not aliased.
+ * moe_recv_ungroup -- the inverse for the return path:
+ *   out[i][:] = grouped[recv_pos[i]][:] for i < N,
+ * after which out is in receive order again and segment s goes back to
+ * source s, landing in exactly the rows that source's combine reads.
+ * Positions outside [0, max_rows) are skipped, never accessed.
+ * Errors: MOE_ERR_INVALID_ARG (pointers, alignment, max_rows < 0),
+ *   MOE_ERR_UNSUPPORTED (H limits, max_rows >= 2^31).
+ */
+moe_status_t moe_recv_regroup(const uint16_t *recv, const int32_t *recv_pos,
+                              const int32_t *n_rows, int64_t max_rows, int32_t H,
+                              uint16_t *grouped, void *stream);
+moe_status_t moe_recv_ungroup(const uint16_t *grouped, const int32_t *recv_pos,
+                              const int32_t *n_rows, int64_t max_rows, int32_t H,
+                              uint16_t *out, void *stream);
+
 /* moe_status_string -- a static, human-readable name for a status. */
 const char *moe_status_string(moe_status_t status);
 

@@ -130,6 +130,52 @@ def test_permute_and_combine_validation(moe):
     assert lib.moe_combine_reduce(None, 0, None, None, None, None, 0, 16, 2, 0, None, None) == moe.MOE_OK
 
 
+def test_regroup_workspace_and_validation(moe):
+    lib = moe.lib
+    assert moe.moe_recv_regroup_workspace_size(64, 8) == (2 * 64 * 8 + 1) * 4
+    assert moe.moe_recv_regroup_workspace_size(1, 1) == 3 * 4
+    assert moe.moe_recv_regroup_workspace_size(4, 1024) == (2 * 4096 + 1) * 4
+    n = ctypes.c_size_t(0)
+    for S, El, want in ((0, 8, moe.MOE_ERR_INVALID_ARG), (8, 0, moe.MOE_ERR_INVALID_ARG),
+                        (1025, 1, moe.MOE_ERR_UNSUPPORTED), (1, 1025, moe.MOE_ERR_UNSUPPORTED),
+                        (128, 64, moe.MOE_ERR_UNSUPPORTED)):
+        assert lib.moe_recv_regroup_workspace_size(S, El, ctypes.byref(n)) == want
+    assert lib.moe_recv_regroup_workspace_size(4, 4, None) == moe.MOE_ERR_INVALID_ARG
+
+    ws = (2 * 4 * 4 + 1) * 4
+
+    def layout(S=4, El=4, cnt=FAKE, leo=FAKE, so=FAKE, rp=FAKE, max_rows=64, w=FAKE, wb=ws):
+        return lib.moe_recv_regroup_layout(cnt, S, El, leo, so, rp, max_rows, w, wb, None)
+
+    assert layout(S=0) == moe.MOE_ERR_INVALID_ARG
+    assert layout(S=2048) == moe.MOE_ERR_UNSUPPORTED
+    assert layout(max_rows=-1) == moe.MOE_ERR_INVALID_ARG
+    assert layout(max_rows=2 ** 31) == moe.MOE_ERR_UNSUPPORTED
+    assert layout(cnt=None) == moe.MOE_ERR_INVALID_ARG
+    assert layout(leo=None) == moe.MOE_ERR_INVALID_ARG
+    assert layout(so=None) == moe.MOE_ERR_INVALID_ARG
+    assert layout(rp=None) == moe.MOE_ERR_INVALID_ARG
+    assert layout(cnt=MIS) == moe.MOE_ERR_INVALID_ARG
+    assert layout(rp=MIS) == moe.MOE_ERR_INVALID_ARG
+    assert layout(w=None) == moe.MOE_ERR_WORKSPACE
+    assert layout(wb=ws - 4) == moe.MOE_ERR_WORKSPACE
+    assert layout(w=FAKE + 4) == moe.MOE_ERR_WORKSPACE
+
+    for fn in (lib.moe_recv_regroup, lib.moe_recv_ungroup):
+        assert fn(FAKE, FAKE, FAKE, 0, 64, FAKE, None) == moe.MOE_OK      # nothing to move
+        assert fn(FAKE, FAKE, FAKE, -1, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+        assert fn(FAKE, FAKE, FAKE, 2 ** 31, 64, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+        assert fn(FAKE, FAKE, FAKE, 16, 60, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+        assert fn(FAKE, FAKE, FAKE, 16, 0, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
+        assert fn(None, FAKE, FAKE, 16, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+        assert fn(FAKE, None, FAKE, 16, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+        assert fn(FAKE, FAKE, None, 16, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+        assert fn(FAKE, FAKE, FAKE, 16, 64, None, None) == moe.MOE_ERR_INVALID_ARG
+        assert fn(FAKE + 8, FAKE, FAKE, 16, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+        assert fn(FAKE, FAKE, FAKE, 16, 64, FAKE + 8, None) == moe.MOE_ERR_INVALID_ARG
+        assert fn(FAKE, MIS, FAKE, 16, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
+
+
 def test_binding_refuses_host_tensors(moe):
     import torch
     with pytest.raises(ValueError):
