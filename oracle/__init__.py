@@ -61,9 +61,18 @@ def _load():
         lib.oracle_bf16_round.argtypes = [ctypes.c_double]
         lib.oracle_bf16_round.restype = ctypes.c_uint16
         lib.oracle_bf16_round_array.argtypes = [P, i64, P]
+        lib.oracle_e4m3_value.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_value.restype = ctypes.c_double
+        lib.oracle_e4m3_round.argtypes = [ctypes.c_double]
+        lib.oracle_fp8_block_exponent.argtypes = [ctypes.c_double]
+        lib.oracle_fp8_quantize_rows.argtypes = [P, i64, i32, P, P]
+        lib.oracle_fp8_dequant_rows.argtypes = [P, P, i64, i32, P]
+        lib.oracle_dispatch_permute_fp8.argtypes = [P, P, i64, i32, i32, P, i64, i64]
         for f in ("oracle_route_topk", "oracle_route_topk_grouped", "oracle_dispatch_layout",
                   "oracle_dispatch_permute", "oracle_combine_reduce", "oracle_recv_regroup_layout",
-                  "oracle_scatter_rows", "oracle_gather_rows"):
+                  "oracle_scatter_rows", "oracle_gather_rows", "oracle_e4m3_round",
+                  "oracle_fp8_block_exponent", "oracle_fp8_quantize_rows", "oracle_fp8_dequant_rows",
+                  "oracle_dispatch_permute_fp8"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -223,3 +232,71 @@ def bf16_to_f64(bits) -> np.ndarray:
     """Exact value of bf16 bit patterns as float64."""
     b = _c(bits, np.uint16)
     return (b.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+# ---------------------------------------------------------------------------
+# FP8 dispatch payload (E4M3 codes, one power-of-two scale byte per 32 values)
+# ---------------------------------------------------------------------------
+
+def e4m3_value(codes) -> np.ndarray:
+    """Value of each E4M3 code (NaN for the NaN codes); oracle_e4m3_value."""
+    c = np.asarray(codes, np.uint8)
+    f = _load().oracle_e4m3_value
+    return np.array([f(int(v)) for v in c.ravel()], np.float64).reshape(c.shape)
+
+
+def e4m3_round(values) -> np.ndarray:
+    """Nearest E4M3 code of each value (|v| <= 448), ties to even; oracle_e4m3_round."""
+    v = np.asarray(values, np.float64)
+    f = _load().oracle_e4m3_round
+    out = np.array([f(float(a)) for a in v.ravel()], np.int32)
+    if np.any(out < 0):
+        raise ValueError("oracle_e4m3_round: value outside the E4M3 range or NaN")
+    return out.astype(np.uint8).reshape(v.shape)
+
+
+def fp8_block_exponent(amax: float) -> int:
+    """Smallest e >= -127 with amax <= 448 * 2^e; oracle_fp8_block_exponent."""
+    return int(_load().oracle_fp8_block_exponent(float(amax)))
+
+
+def fp8_quantize_rows(x: np.ndarray):
+    """(codes [n, H] uint8, scale bytes [n, H/32] uint8) of bf16 rows x [n, H]."""
+    x = _c(x, np.uint16)
+    n, H = x.shape
+    codes = np.empty((n, H), np.uint8)
+    scales = np.empty((n, max(H // 32, 1)), np.uint8)
+    if _load().oracle_fp8_quantize_rows(_ptr(x), n, H, _ptr(codes), _ptr(scales)) != 0:
+        raise ValueError("oracle_fp8_quantize_rows: H % 32 != 0 or a non-finite value")
+    return codes, scales
+
+
+def fp8_dequant_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    """bf16 bits of value(code) * 2^(scale - 127), ties to even."""
+    codes = _c(codes, np.uint8)
+    scales = _c(scales, np.uint8)
+    n, H = codes.shape
+    out = np.empty((n, H), np.uint16)
+    if _load().oracle_fp8_dequant_rows(_ptr(codes), _ptr(scales), n, H, _ptr(out)) != 0:
+        raise ValueError("oracle_fp8_dequant_rows: H % 32 != 0 or a NaN code")
+    return out
+
+
+def fp8_row_bytes(H: int) -> int:
+    """Bytes of one FP8 send row: H codes, H/32 scale bytes, padded to 16."""
+    return H + (H // 32 + 15) // 16 * 16
+
+
+def dispatch_permute_fp8(x: np.ndarray, pos: np.ndarray, send_rows: int, row_bytes: Optional[int] = None,
+                         fill: int = 0) -> np.ndarray:
+    """FP8 send buffer [send_rows, row_bytes] uint8: row pos[t][j] holds the
+    codes then the scale bytes of x[t]; other bytes hold `fill`."""
+    x = _c(x, np.uint16)
+    pos = _c(pos, np.int32)
+    T, H = x.shape
+    k = pos.shape[1]
+    rb = fp8_row_bytes(H) if row_bytes is None else row_bytes
+    send = np.full((send_rows, rb), fill, np.uint8)
+    if _load().oracle_dispatch_permute_fp8(_ptr(x), _ptr(pos), T, H, k, _ptr(send), send_rows, rb) != 0:
+        raise ValueError("oracle_dispatch_permute_fp8 rejected its arguments")
+    return send

@@ -32,6 +32,9 @@
  *    factor, excess dropped; ragged routing is dropless.
  *  - ai-from-scratch "19. All-to-all", section on 512 experts (10 routed +
  *    1 shared): the shared expert is always active.
+ *  - aicassindra "gpu_moe_all_to_all", "Latency-bound at decode,
+ *    bandwidth-bound at prefill": a lower-precision dispatch payload (the
+ *    FP8 section below states the reading taken for its format).
  *
  * Build: gcc -std=c11 -O2 -ffp-contract=off -fno-fast-math -shared -fPIC.
  * Parity pins for every function live in the CPU test suite; none of the
@@ -531,6 +534,159 @@ int oracle_combine_reduce(const uint16_t *y, int64_t y_rows, const int32_t *pos,
             if (residual)
                 acc += bf16_value(residual[t * (int64_t)H + h]);
             out[i * (int64_t)H + h] = acc;
+        }
+    }
+    return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* FP8 dispatch payload: E4M3 codes with one power-of-two scale per 32 */
+/* ------------------------------------------------------------------ */
+
+/*
+ * The pages name a smaller dispatch payload as the first lever once the
+ * exchange is bandwidth-bound, because the expert matmul casts its input to
+ * a lower precision anyway (aicassindra "gpu_moe_all_to_all", "Latency-bound
+ * at decode, bandwidth-bound at prefill"; zenaique Q&A
+ * "moe-hide-alltoall-techniques", the third family of fixes: shrink the
+ * payload). They fix neither the format nor the scaling, so this oracle
+ * takes the reading stated next.
+ *
+ * Element format: OCP 8-bit floating point E4M3 (1 sign, 4 exponent bits
+ * with bias 7, 3 mantissa bits, subnormals, no infinities; S.1111.111 is
+ * NaN), largest finite value 448. Scale: one power of two 2^e per block of
+ * 32 consecutive values along H, stored as its biased exponent e + 127 in
+ * one byte (the E8M0 encoding of the OCP microscaling formats). For a block
+ * with largest magnitude a, e is the smallest integer >= -127 with
+ * a <= 448 * 2^e, so no value of the block saturates. Each code is the
+ * E4M3 value nearest to x / 2^e (ties to the even code); x / 2^e is exact
+ * in any binary format wide enough, so the choice does not depend on the
+ * precision it is computed in. Decoding multiplies the code's value by 2^e.
+ */
+
+/* Value of an E4M3 code (NaN for S.1111.111). */
+double oracle_e4m3_value(uint8_t code)
+{
+    int s = code >> 7, E = (code >> 3) & 0xF, m = code & 7;
+    if (E == 15 && m == 7)
+        return NAN;
+    double mag = E == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, E - 7);
+    return s ? -mag : mag;
+}
+
+/*
+ * Nearest E4M3 code to v, ties to the code with an even last bit, found by
+ * comparing v with every finite non-negative code; the sign is kept (a
+ * negative value that rounds to zero gives -0). Returns -1 when |v| > 448
+ * or v is NaN.
+ */
+int oracle_e4m3_round(double v)
+{
+    if (isnan(v) || fabs(v) > 448.0)
+        return -1;
+    double a = fabs(v);
+    int best = 0;
+    double best_d = a;
+    for (int c = 1; c <= 0x7E; ++c) {
+        double d = fabs(a - oracle_e4m3_value((uint8_t)c));
+        if (d < best_d || (d == best_d && (c & 1) == 0)) {
+            best = c;
+            best_d = d;
+        }
+    }
+    return (signbit(v) ? 0x80 : 0) | best;
+}
+
+/* Smallest e >= -127 with amax <= 448 * 2^e (amax finite, >= 0). */
+int oracle_fp8_block_exponent(double amax)
+{
+    int e = -127;
+    while (amax > ldexp(448.0, e))
+        ++e;
+    return e;
+}
+
+static int is_finite_bf16(uint16_t bits) { return (bits & 0x7F80u) != 0x7F80u; }
+
+/* Codes and scale bytes of one row of H bf16 values (H % 32 == 0). */
+static int quantize_row(const uint16_t *x, int32_t H, uint8_t *codes, uint8_t *scales)
+{
+    for (int32_t b = 0; b < H / 32; ++b) {
+        double amax = 0.0;
+        for (int32_t i = 0; i < 32; ++i) {
+            if (!is_finite_bf16(x[b * 32 + i]))
+                return -1;
+            double a = fabs(bf16_value(x[b * 32 + i]));
+            if (a > amax)
+                amax = a;
+        }
+        int e = oracle_fp8_block_exponent(amax);
+        scales[b] = (uint8_t)(e + 127);
+        for (int32_t i = 0; i < 32; ++i)
+            codes[b * 32 + i] = (uint8_t)oracle_e4m3_round(ldexp(bf16_value(x[b * 32 + i]), -e));
+    }
+    return 0;
+}
+
+/*
+ * codes[r][:] and scales[r][:] (H / 32 bytes) of rows r < n of x.
+ * Returns -1 when H % 32 != 0 or a row holds a NaN or an infinity (the
+ * reading above leaves those unspecified).
+ */
+int oracle_fp8_quantize_rows(const uint16_t *x, int64_t n, int32_t H, uint8_t *codes,
+                             uint8_t *scales)
+{
+    if (H <= 0 || H % 32 != 0)
+        return -1;
+    for (int64_t r = 0; r < n; ++r)
+        if (quantize_row(x + r * H, H, codes + r * H, scales + r * (H / 32)) != 0)
+            return -1;
+    return 0;
+}
+
+/*
+ * out[r][h] = bf16 nearest to value(codes[r][h]) * 2^(scales[r][h / 32] - 127),
+ * ties to even. Returns -1 when H % 32 != 0 or a code is NaN.
+ */
+int oracle_fp8_dequant_rows(const uint8_t *codes, const uint8_t *scales, int64_t n, int32_t H,
+                            uint16_t *out)
+{
+    if (H <= 0 || H % 32 != 0)
+        return -1;
+    for (int64_t r = 0; r < n; ++r)
+        for (int32_t h = 0; h < H; ++h) {
+            double v = oracle_e4m3_value(codes[r * H + h]);
+            if (isnan(v))
+                return -1;
+            int e = (int)scales[r * (H / 32) + h / 32] - 127;
+            out[r * H + h] = oracle_bf16_round(ldexp(v, e));
+        }
+    return 0;
+}
+
+/*
+ * FP8 dispatch permute: for every kept (t, j), send row pos[t][j] (row_bytes
+ * bytes, row_bytes >= H + H / 32) holds the H codes of x[t] followed by its
+ * H / 32 scale bytes; bytes past H + H / 32 and rows no assignment points
+ * at are left as they were. Returns -1 on a position outside
+ * [0, send_rows), a short row, H % 32 != 0 or a non-finite x value of a
+ * kept token.
+ */
+int oracle_dispatch_permute_fp8(const uint16_t *x, const int32_t *pos, int64_t T, int32_t H,
+                                int32_t k, uint8_t *send, int64_t send_rows, int64_t row_bytes)
+{
+    if (H <= 0 || H % 32 != 0 || row_bytes < H + H / 32)
+        return -1;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t j = 0; j < k; ++j) {
+            int32_t p = pos[t * k + j];
+            if (p < 0)
+                continue;
+            if (p >= send_rows)
+                return -1;
+            uint8_t *row = send + (int64_t)p * row_bytes;
+            if (quantize_row(x + t * (int64_t)H, H, row, row + H) != 0)
+                return -1;
         }
     }
     return 0;

@@ -14,7 +14,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PIN_TESTS = ["tests/test_oracle_route.py", "tests/test_oracle_layout.py", "tests/test_oracle_combine.py",
-             "tests/test_oracle_regroup.py"]
+             "tests/test_oracle_regroup.py", "tests/test_oracle_fp8.py"]
 
 MUTATIONS = {
     "tie_break_to_higher_id": ("    return ia < ib;\n", "    return ia > ib;\n"),
@@ -42,6 +42,16 @@ MUTATIONS = {
     "regroup_counts_earlier_experts": ("                before += cnt[s2 * E_l + l];", "                before += cnt[src * E_l + s2 % E_l];"),
     "regroup_expert_base_off_by_one": ("                recv_pos[i++] = local_expert_offsets[l] + before + j;",
                                        "                recv_pos[i++] = local_expert_offsets[l] + before + j + (l > 0);"),
+    "e4m3_ties_to_odd": ("(d == best_d && (c & 1) == 0)", "(d == best_d && (c & 1) == 1)"),
+    "e4m3_subnormal_spacing": ("ldexp((double)m, -9)", "ldexp((double)m, -10)"),
+    "e4m3_exponent_bias": ("ldexp(1.0 + m / 8.0, E - 7)", "ldexp(1.0 + m / 8.0, E - 8)"),
+    "fp8_scale_one_too_large_at_the_edge": ("while (amax > ldexp(448.0, e))", "while (amax >= ldexp(448.0, e))"),
+    "fp8_scale_for_256": ("while (amax > ldexp(448.0, e))", "while (amax > ldexp(256.0, e))"),
+    "fp8_dequant_scale_bias": ("int e = (int)scales[r * (H / 32) + h / 32] - 127;",
+                               "int e = (int)scales[r * (H / 32) + h / 32] - 126;"),
+    "fp8_amax_ignores_sign": ("double a = fabs(bf16_value(x[b * 32 + i]));", "double a = bf16_value(x[b * 32 + i]);"),
+    "fp8_permute_scales_misplaced": ("quantize_row(x + t * (int64_t)H, H, row, row + H)",
+                                     "quantize_row(x + t * (int64_t)H, H, row, row + H + 1)"),
     "bf16_ties_away_from_zero": ("double r = nearbyint(a / q) * q;", "double r = round(a / q) * q;"),
     "bf16_no_subnormal_spacing": ("if (e < -126)\n        e = -126;", "if (e < -140)\n        e = -140;"),
 }
