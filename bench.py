@@ -20,9 +20,11 @@ for kept rows only:
 with N kept rows and T_read tokens that have at least one kept replica (both
 read from the path's own outputs after the timed region).
 
-After the path, the receive-side regroup is timed on the same buffers (the
-send buffer read as R source segments) and reported under "next_rows"; it
-is not part of `value`.
+After the path, two further measurements are reported under "next_rows",
+neither part of `value`: the same step with the FP8 dispatch payload
+(moe_dispatch_permute_fp8 in place of the bf16 permute), and the
+receive-side regroup on the same buffers (the send buffer read as R source
+segments).
 
 The CPU-baseline leg times the plain C oracle on the same host arrays.
 """
@@ -65,6 +67,8 @@ def parse():
     p.add_argument("--workload", default="fine_grained",
                    help="one of " + ", ".join(w.name for w in synthetic.WORKLOADS.values()))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-fp8", action="store_true",
+                   help="skip the FP8-payload step measurement (reported under next_rows)")
     p.add_argument("--no-regroup", action="store_true",
                    help="skip the receive-side regroup measurement (reported under next_rows)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -180,6 +184,75 @@ def bench_regroup(moe, torch, lay, send, S, El, H, rows, stream, warmup, steps):
                         "frac": round(gbps["regroup"] / HBM_PEAK_GBPS, 4), "algorithmic_bytes": nb["regroup"]}}
     log("regroup", out)
     return out
+
+
+def bench_fp8(moe, torch, calls, lay, x, wt, sh, res, T, H, E, k, send_rows, nbytes, stream,
+              warmup, steps):
+    """The step with the FP8 dispatch payload: route -> layout ->
+    moe_dispatch_permute_fp8 -> combine. The expert is the identity on the
+    decoded rows: y = moe_fp8_dequant(send) is made once, before timing (a
+    real expert matmul reads the FP8 rows itself and writes bf16 y).
+    Algorithmic bytes of the FP8 permute: T*k*4 + T_read*H*2 + N*row_bytes."""
+    dev = x.device
+    rb = moe.moe_fp8_row_bytes(H)
+    send8 = torch.empty((send_rows, rb), dtype=torch.uint8, device=dev)
+    y = torch.empty((send_rows, H), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    sp = stream.cuda_stream
+    lib, P = moe.lib, (lambda t: None if t is None else t.data_ptr())
+
+    def check(name, rc):
+        if rc != moe.MOE_OK:
+            raise RuntimeError(f"{name}: {moe.moe_status_string(rc)}")
+
+    fcalls = calls[:2] + [
+        ("permute_fp8", lambda: check("permute_fp8", lib.moe_dispatch_permute_fp8(
+            P(x), P(lay["pos"]), T, H, k, P(send8), send_rows, sp))),
+        ("combine", lambda: check("combine", lib.moe_combine_reduce(
+            P(y), send_rows, P(lay["pos"]), P(wt), P(sh), P(res), T, H, k, 0, P(out), sp))),
+    ]
+    for _, fn in fcalls[:3]:
+        fn()
+    check("fp8 dequant", lib.moe_fp8_dequant(P(send8), P(lay["expert_offsets"][E:]), send_rows, H,
+                                             P(y), sp))
+    for _ in range(warmup):
+        for _, fn in fcalls:
+            fn()
+    torch.cuda.synchronize()
+    beg, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    beg.record(stream)
+    for _ in range(steps):
+        for _, fn in fcalls:
+            fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_step = beg.elapsed_time(end) / steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fcalls) + 1)] for _ in range(steps)]
+    for s in range(steps):
+        for i, (_, fn) in enumerate(fcalls):
+            ev[s][i].record(stream)
+            fn()
+        ev[s][len(fcalls)].record(stream)
+    torch.cuda.synchronize()
+    us = {name: statistics.mean(ev[s][i].elapsed_time(ev[s][i + 1]) for s in range(steps)) * 1e3
+          for i, (name, _) in enumerate(fcalls)}
+    N = int(lay["expert_offsets"][E].item())
+    T_read = int((lay["pos"] >= 0).any(dim=1).sum().item())
+    nb = dict(nbytes)
+    del nb["permute"]
+    nb["permute_fp8"] = T * k * 4 + T_read * H * 2 + N * rb
+    total = sum(nb.values())
+    gbps_p = nb["permute_fp8"] / (us["permute_fp8"] * 1e-6) / 1e9
+    report = {"row_bytes": rb, "bytes_per_step": total, "us_per_step": round(ms_step * 1e3, 2),
+           "GBps": round(total / (ms_step * 1e-3) / 1e9, 1), "tokens_per_s": round(T / (ms_step * 1e-3), 1),
+           "per_call_us": {n: round(v, 2) for n, v in us.items()},
+           "roofline": {"bound": "hbm", "kernel": "permute_fp8_kernel", "achieved": round(gbps_p, 1),
+                        "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps_p / HBM_PEAK_GBPS, 4),
+                        "algorithmic_bytes": nb["permute_fp8"]},
+           "note": "send rows hold E4M3 codes plus one scale byte per 32 values; combine reads the "
+                   "identity expert's bf16 output, decoded once before timing"}
+    log("fp8 dispatch", report)
+    return report
 
 
 def cpu_baseline(w, d, budget_s):
@@ -323,6 +396,9 @@ def main():
                 "kernel": kname, "algorithmic_bytes": nbytes[dominant],
                 "avg_launch_us": round(per_call_ms[dominant] * 1e3, 2)}
 
+    fp8 = None if args.no_fp8 or H % 32 else bench_fp8(
+        moe, torch, calls, lay, x, wt, sh, res, T, H, E, k, send_rows, nbytes, stream,
+        args.warmup, args.steps)
     regroup = None if args.no_regroup or R < 2 else bench_regroup(
         moe, torch, lay, send, R, E // R, H, send_rows, stream, args.warmup, args.steps)
 
@@ -369,8 +445,13 @@ def main():
         "per_call_GBps": {n: round(nbytes[n] / (per_call_ms[n] * 1e-3) / 1e9, 1) for n in nbytes},
         "roofline": roofline,
     }
+    next_rows = {}
+    if fp8:
+        next_rows["fp8_dispatch"] = fp8
     if regroup:
-        result["next_rows"] = {"recv_regroup": regroup}
+        next_rows["recv_regroup"] = regroup
+    if next_rows:
+        result["next_rows"] = next_rows
     if copy_probe:
         result["copy_probe"] = copy_probe
 

@@ -29,7 +29,8 @@ MOE_ROUTE_NORMALIZE = 1
 MOE_COMBINE_OUT_FP32 = 1
 
 EXPORTS = ("moe_route_topk", "moe_route_topk_grouped", "moe_layout_workspace_size", "moe_dispatch_layout",
-           "moe_dispatch_permute", "moe_combine_reduce", "moe_recv_regroup_workspace_size",
+           "moe_dispatch_permute", "moe_combine_reduce", "moe_fp8_row_bytes",
+           "moe_dispatch_permute_fp8", "moe_fp8_dequant", "moe_recv_regroup_workspace_size",
            "moe_recv_regroup_layout", "moe_recv_regroup", "moe_recv_ungroup", "moe_status_string")
 
 
@@ -53,6 +54,9 @@ def _load_library() -> ctypes.CDLL:
                                         ctypes.c_size_t, P]
     lib.moe_dispatch_permute.argtypes = [P, P, i64, i32, i32, P, i64, P]
     lib.moe_combine_reduce.argtypes = [P, i64, P, P, P, P, i64, i32, i32, u32, P, P]
+    lib.moe_fp8_row_bytes.argtypes = [i32, ctypes.POINTER(ctypes.c_int64)]
+    lib.moe_dispatch_permute_fp8.argtypes = [P, P, i64, i32, i32, P, i64, P]
+    lib.moe_fp8_dequant.argtypes = [P, P, i64, i32, P, P]
     lib.moe_recv_regroup_workspace_size.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.moe_recv_regroup_layout.argtypes = [P, i32, i32, P, P, P, i64, P, ctypes.c_size_t, P]
     lib.moe_recv_regroup.argtypes = [P, P, P, i64, i32, P, P]
@@ -261,4 +265,41 @@ def moe_recv_ungroup(grouped: torch.Tensor, recv_pos: torch.Tensor, n_rows: torc
     _check("moe_recv_ungroup", lib.moe_recv_ungroup(
         _ptr(grouped, _BF16, "grouped", 2), _ptr(recv_pos, _I32, "recv_pos"), _ptr(n_rows, _I32, "n_rows"),
         rows, H, _ptr(out, _BF16, "out"), _stream(stream)))
+    return out
+
+
+def moe_fp8_row_bytes(H: int) -> int:
+    n = ctypes.c_int64(0)
+    _check("moe_fp8_row_bytes", lib.moe_fp8_row_bytes(H, ctypes.byref(n)))
+    return n.value
+
+
+def moe_dispatch_permute_fp8(x: torch.Tensor, pos: torch.Tensor, send_rows: int,
+                             send: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """FP8 send buffer [send_rows, moe_fp8_row_bytes(H)] uint8: row pos[t][j]
+    holds x[t]'s E4M3 codes then its scale bytes (see moe_dispatch_permute_fp8)."""
+    T, H = x.shape
+    k = pos.shape[1]
+    rb = moe_fp8_row_bytes(H)
+    if send is None:
+        send = torch.empty((send_rows, rb), dtype=torch.uint8, device=x.device)
+    elif send.dim() != 2 or send.shape[1] != rb or send.shape[0] < send_rows:
+        raise ValueError(f"send must be [>= {send_rows}, {rb}] bytes, got {tuple(send.shape)}")
+    _check("moe_dispatch_permute_fp8", lib.moe_dispatch_permute_fp8(
+        _ptr(x, _BF16, "x", 2), _ptr(pos, _I32, "pos", 2), T, H, k,
+        _ptr(send, (torch.uint8,), "send", 2), send_rows, _stream(stream)))
+    return send
+
+
+def moe_fp8_dequant(rows: torch.Tensor, H: int, n_rows: Optional[torch.Tensor] = None,
+                    out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """bf16 [max_rows, H] decoded from FP8 rows (rows past *n_rows untouched)."""
+    max_rows = rows.shape[0]
+    if rows.dim() != 2 or rows.shape[1] != moe_fp8_row_bytes(H):
+        raise ValueError(f"rows must be [n, {moe_fp8_row_bytes(H)}] bytes, got {tuple(rows.shape)}")
+    if out is None:
+        out = torch.empty((max_rows, H), dtype=torch.bfloat16, device=rows.device)
+    _check("moe_fp8_dequant", lib.moe_fp8_dequant(
+        _ptr(rows, (torch.uint8,), "rows", 2), None if n_rows is None else _ptr(n_rows, _I32, "n_rows"),
+        max_rows, H, _ptr(out, _BF16, "out", 2), _stream(stream)))
     return out

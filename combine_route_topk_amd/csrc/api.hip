@@ -198,6 +198,64 @@ moe_status_t moe_dispatch_permute(const uint16_t *x, const int32_t *pos, int64_t
                                                  static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_fp8_row_bytes(int32_t H, int64_t *bytes)
+{
+    if (!bytes)
+        return MOE_ERR_INVALID_ARG;
+    moe_status_t s = check_hidden(H);
+    if (s != MOE_OK)
+        return s;
+    if (H % 32 != 0)
+        return MOE_ERR_UNSUPPORTED;
+    *bytes = moe::fp8_row_bytes(H);
+    return MOE_OK;
+}
+
+moe_status_t moe_dispatch_permute_fp8(const uint16_t *x, const int32_t *pos, int64_t T,
+                                      int32_t H, int32_t k, uint8_t *send, int64_t send_rows,
+                                      void *stream)
+{
+    moe_status_t s = check_tokens(T, k);
+    if (s != MOE_OK)
+        return s;
+    if ((s = check_hidden(H)) != MOE_OK)
+        return s;
+    if (H % 32 != 0)
+        return MOE_ERR_UNSUPPORTED;
+    if (send_rows < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (T == 0)
+        return MOE_OK;
+    if (!x || !pos || (!send && send_rows > 0))
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(x, 16) || !aligned(send, 16) || !aligned(pos, 4))
+        return MOE_ERR_INVALID_ARG;
+    return from_hip(moe::launch_dispatch_permute_fp8(x, pos, T, H, k, send, send_rows,
+                                                     static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_fp8_dequant(const uint8_t *rows, const int32_t *n_rows, int64_t max_rows,
+                             int32_t H, uint16_t *out, void *stream)
+{
+    if (max_rows < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (max_rows >= kMaxAssignments)
+        return MOE_ERR_UNSUPPORTED;
+    moe_status_t s = check_hidden(H);
+    if (s != MOE_OK)
+        return s;
+    if (H % 32 != 0)
+        return MOE_ERR_UNSUPPORTED;
+    if (max_rows == 0)
+        return MOE_OK;
+    if (!rows || !out)
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(rows, 16) || !aligned(out, 16) || !aligned(n_rows, 4))
+        return MOE_ERR_INVALID_ARG;
+    return from_hip(moe::launch_fp8_dequant(rows, n_rows, max_rows, H, out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
 moe_status_t moe_combine_reduce(const uint16_t *y, int64_t y_rows, const int32_t *pos,
                                 const float *topk_w, const uint16_t *shared,
                                 const uint16_t *residual, int64_t T, int32_t H, int32_t k,

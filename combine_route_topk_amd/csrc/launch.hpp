@@ -53,6 +53,14 @@ hipError_t launch_combine_reduce(const uint16_t *y, int64_t y_rows, const int32_
                                  const uint16_t *residual, int64_t T, int32_t H, int32_t k,
                                  bool out_fp32, void *out, hipStream_t stream);
 
+// FP8 dispatch payload (fp8.hip).
+int64_t fp8_row_bytes(int32_t H);
+hipError_t launch_dispatch_permute_fp8(const uint16_t *x, const int32_t *pos, int64_t T,
+                                       int32_t H, int32_t k, uint8_t *send, int64_t send_rows,
+                                       hipStream_t stream);
+hipError_t launch_fp8_dequant(const uint8_t *rows, const int32_t *n_rows, int64_t max_rows,
+                              int32_t H, uint16_t *out, hipStream_t stream);
+
 // Receive-side regroup (regroup.hip).
 size_t regroup_workspace_bytes(int32_t S, int32_t El);
 hipError_t launch_recv_regroup_layout(const int32_t *recv_counts, int32_t S, int32_t El,

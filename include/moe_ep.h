@@ -245,6 +245,59 @@ moe_status_t moe_combine_reduce(const uint16_t *y, int64_t y_rows,
                                 void *out, void *stream);
 
 /*
+ * FP8 dispatch payload: the permute quantises each row as it packs it, so
+ * the send buffer holds about half the bytes of the bf16 one.
+ *
+ * Defined by: aicassindra "gpu_moe_all_to_all", "Latency-bound at decode,
+ * bandwidth-bound at prefill" (send fewer bytes: a lower-precision dispatch
+ * payload, because the expert matmul casts its input anyway) and
+ * "Bucketing" (the permutation fused into the staging kernel); zenaique Q&A
+ * "moe-hide-alltoall-techniques" (shrink the payload). The pages fix no
+ * format; this library's reading:
+ *   - codes: OCP FP8 E4M3 (bias 7, largest finite 448, no infinities);
+ *   - scales: one power of two 2^e per 32 consecutive values of a row,
+ *     stored as the byte e + 127 (E8M0); e is the smallest integer >= -127
+ *     with max|x| <= 448 * 2^e, so no value saturates;
+ *   - code = the E4M3 value nearest to x / 2^e, ties to even (x / 2^e is
+ *     exact, so the code does not depend on arithmetic precision);
+ *   - a send row: H code bytes, then one 128-byte line per 4096 values
+ *     holding that slab's 128 scale bytes, zero-padded in the last slab:
+ *     moe_fp8_row_bytes(H) = H + 128 * ceil(H / 4096). For H % 128 == 0
+ *     rows start on 128-byte lines and are written in whole lines; a
+ *     destination's segment is still one contiguous range of rows.
+ * NaN or infinite inputs give unspecified codes and scales.
+ */
+
+/* Bytes of one FP8 send row (written to *bytes). Needs H % 32 == 0. */
+moe_status_t moe_fp8_row_bytes(int32_t H, int64_t *bytes);
+
+/*
+ * moe_dispatch_permute_fp8 -- as moe_dispatch_permute, but row pos[t][j] of
+ * send ([send_rows][moe_fp8_row_bytes(H)] bytes, 16-byte aligned) receives
+ * the FP8 codes, scale bytes and zero padding of x[t]. Rows no kept
+ * assignment points at are left as they were.
+ * Errors: as moe_dispatch_permute; MOE_ERR_UNSUPPORTED when H % 32 != 0.
+ */
+moe_status_t moe_dispatch_permute_fp8(const uint16_t *x, const int32_t *pos, int64_t T,
+                                      int32_t H, int32_t k, uint8_t *send,
+                                      int64_t send_rows, void *stream);
+
+/*
+ * moe_fp8_dequant -- decode FP8 rows to bf16 (for an expert that takes
+ * bf16, or to check a payload):
+ *   out[i][h] = bf16 nearest to value(code[i][h]) * 2^(scale[i][h/32] - 127)
+ * (ties to even; exact unless below bf16's subnormal spacing) for
+ * i < min(*n_rows, max_rows), or i < max_rows when n_rows is NULL (n_rows
+ * is a device pointer, e.g. expert_offsets + E). rows: [max_rows]
+ * [moe_fp8_row_bytes(H)] bytes; out: [max_rows][H] bf16; both 16-byte
+ * aligned. NaN codes give unspecified values.
+ * Errors: MOE_ERR_INVALID_ARG (pointers, alignment, max_rows < 0),
+ *   MOE_ERR_UNSUPPORTED (H limits, H % 32 != 0, max_rows >= 2^31).
+ */
+moe_status_t moe_fp8_dequant(const uint8_t *rows, const int32_t *n_rows, int64_t max_rows,
+                             int32_t H, uint16_t *out, void *stream);
+
+/*
  * Receive side: regroup a destination's receive buffer into expert-major
  * rows for the expert computation, and back for the return path.
  *

@@ -283,14 +283,15 @@ def fp8_dequant_rows(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
 
 
 def fp8_row_bytes(H: int) -> int:
-    """Bytes of one FP8 send row: H codes, H/32 scale bytes, padded to 16."""
-    return H + (H // 32 + 15) // 16 * 16
+    """Bytes of one FP8 send row: H codes, then one 128-byte line per 4096
+    values holding that slab's 128 scale bytes (zero-padded in the last)."""
+    return H + 128 * ((H + 4095) // 4096)
 
 
 def dispatch_permute_fp8(x: np.ndarray, pos: np.ndarray, send_rows: int, row_bytes: Optional[int] = None,
                          fill: int = 0) -> np.ndarray:
     """FP8 send buffer [send_rows, row_bytes] uint8: row pos[t][j] holds the
-    codes then the scale bytes of x[t]; other bytes hold `fill`."""
+    codes, the scale bytes and zero padding of x[t]; other rows hold `fill`."""
     x = _c(x, np.uint16)
     pos = _c(pos, np.int32)
     T, H = x.shape

@@ -666,11 +666,10 @@ int oracle_fp8_dequant_rows(const uint8_t *codes, const uint8_t *scales, int64_t
 
 /*
  * FP8 dispatch permute: for every kept (t, j), send row pos[t][j] (row_bytes
- * bytes, row_bytes >= H + H / 32) holds the H codes of x[t] followed by its
- * H / 32 scale bytes; bytes past H + H / 32 and rows no assignment points
- * at are left as they were. Returns -1 on a position outside
- * [0, send_rows), a short row, H % 32 != 0 or a non-finite x value of a
- * kept token.
+ * bytes, row_bytes >= H + H / 32) holds the H codes of x[t], then its H / 32
+ * scale bytes, then zero bytes up to row_bytes. Rows no assignment points at
+ * are left as they were. Returns -1 on a position outside [0, send_rows), a
+ * short row, H % 32 != 0 or a non-finite x value of a kept token.
  */
 int oracle_dispatch_permute_fp8(const uint16_t *x, const int32_t *pos, int64_t T, int32_t H,
                                 int32_t k, uint8_t *send, int64_t send_rows, int64_t row_bytes)
@@ -687,6 +686,8 @@ int oracle_dispatch_permute_fp8(const uint16_t *x, const int32_t *pos, int64_t T
             uint8_t *row = send + (int64_t)p * row_bytes;
             if (quantize_row(x + t * (int64_t)H, H, row, row + H) != 0)
                 return -1;
+            for (int64_t b = H + H / 32; b < row_bytes; ++b)
+                row[b] = 0;
         }
     }
     return 0;

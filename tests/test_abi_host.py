@@ -176,6 +176,51 @@ def test_regroup_workspace_and_validation(moe):
         assert fn(FAKE, MIS, FAKE, 16, 64, FAKE, None) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_fp8_validation(moe):
+    lib = moe.lib
+    assert moe.moe_fp8_row_bytes(2048) == 2048 + 128      # one scale line per 4096 values
+    assert moe.moe_fp8_row_bytes(4096) == 4096 + 128
+    assert moe.moe_fp8_row_bytes(7168) == 7168 + 256
+    assert moe.moe_fp8_row_bytes(96) == 96 + 128
+    assert moe.moe_fp8_row_bytes(65536) == 65536 + 16 * 128
+    import oracle
+    for H in (32, 96, 2048, 4096, 4128, 7168, 65536):
+        assert moe.moe_fp8_row_bytes(H) == oracle.fp8_row_bytes(H)
+    n = ctypes.c_int64(0)
+    assert lib.moe_fp8_row_bytes(48, ctypes.byref(n)) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_fp8_row_bytes(0, ctypes.byref(n)) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_fp8_row_bytes(64, None) == moe.MOE_ERR_INVALID_ARG
+
+    def perm(x=FAKE, pos=FAKE, T=16, H=64, k=2, send=FAKE, rows=32):
+        return lib.moe_dispatch_permute_fp8(x, pos, T, H, k, send, rows, None)
+
+    assert perm(T=-1) == moe.MOE_ERR_INVALID_ARG
+    assert perm(k=0) == moe.MOE_ERR_UNSUPPORTED
+    assert perm(H=48) == moe.MOE_ERR_UNSUPPORTED
+    assert perm(H=40) == moe.MOE_ERR_UNSUPPORTED
+    assert perm(rows=-1) == moe.MOE_ERR_INVALID_ARG
+    assert perm(T=0) == moe.MOE_OK
+    assert perm(x=None) == moe.MOE_ERR_INVALID_ARG
+    assert perm(pos=None) == moe.MOE_ERR_INVALID_ARG
+    assert perm(send=None) == moe.MOE_ERR_INVALID_ARG
+    assert perm(x=FAKE + 8) == moe.MOE_ERR_INVALID_ARG
+    assert perm(send=FAKE + 8) == moe.MOE_ERR_INVALID_ARG
+    assert perm(pos=MIS) == moe.MOE_ERR_INVALID_ARG
+
+    def deq(rows=FAKE, n=FAKE, max_rows=16, H=64, out=FAKE):
+        return lib.moe_fp8_dequant(rows, n, max_rows, H, out, None)
+
+    assert deq(max_rows=0) == moe.MOE_OK
+    assert deq(max_rows=-1) == moe.MOE_ERR_INVALID_ARG
+    assert deq(max_rows=2 ** 31) == moe.MOE_ERR_UNSUPPORTED
+    assert deq(H=48) == moe.MOE_ERR_UNSUPPORTED
+    assert deq(rows=None) == moe.MOE_ERR_INVALID_ARG
+    assert deq(out=None) == moe.MOE_ERR_INVALID_ARG
+    assert deq(rows=FAKE + 8) == moe.MOE_ERR_INVALID_ARG
+    assert deq(out=FAKE + 8) == moe.MOE_ERR_INVALID_ARG
+    assert deq(n=MIS) == moe.MOE_ERR_INVALID_ARG
+
+
 def test_binding_refuses_host_tensors(moe):
     import torch
     with pytest.raises(ValueError):

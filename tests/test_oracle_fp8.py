@@ -185,8 +185,8 @@ def test_golden_block(orc):
 
 
 def test_permute_fp8_is_quantised_permute(orc):
-    """Row pos[t][j] holds quantize(x[t]) codes then scale bytes; dropped
-    replicas and untouched rows keep the fill; padding bytes too."""
+    """Row pos[t][j] holds quantize(x[t]) codes, then scale bytes, then zero
+    padding; dropped replicas leave their rows (and rows past N) at the fill."""
     r = np.random.default_rng(8)
     T, H, E, k, R = 40, 96, 8, 3, 2
     x = bf16_rows(r, T, H)
@@ -198,7 +198,7 @@ def test_permute_fp8_is_quantised_permute(orc):
     rows = N + 3
     send = orc.dispatch_permute_fp8(x, L["pos"], rows, fill=0xA5)
     rb = orc.fp8_row_bytes(H)
-    assert rb == 96 + 16 and send.shape == (rows, rb)
+    assert rb == 96 + 128 and send.shape == (rows, rb)
     codes, scales = orc.fp8_quantize_rows(x)
     for t in range(T):
         for j in range(k):
@@ -206,7 +206,7 @@ def test_permute_fp8_is_quantised_permute(orc):
             if p >= 0:
                 np.testing.assert_array_equal(send[p, :H], codes[t])
                 np.testing.assert_array_equal(send[p, H:H + H // 32], scales[t])
-    assert np.all(send[:, H + H // 32:] == 0xA5)
+    assert np.all(send[:N, H + H // 32:] == 0)
     assert np.all(send[N:] == 0xA5)
     # same rows as quantising the bf16 send buffer
     bf = orc.dispatch_permute(x, L["pos"], N)

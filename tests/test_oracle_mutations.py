@@ -50,6 +50,8 @@ MUTATIONS = {
     "fp8_dequant_scale_bias": ("int e = (int)scales[r * (H / 32) + h / 32] - 127;",
                                "int e = (int)scales[r * (H / 32) + h / 32] - 126;"),
     "fp8_amax_ignores_sign": ("double a = fabs(bf16_value(x[b * 32 + i]));", "double a = bf16_value(x[b * 32 + i]);"),
+    "fp8_permute_padding_not_cleared": ("            for (int64_t b = H + H / 32; b < row_bytes; ++b)\n                row[b] = 0;",
+                                        "            for (int64_t b = H + H / 32 + 1; b < row_bytes; ++b)\n                row[b] = 0;"),
     "fp8_permute_scales_misplaced": ("quantize_row(x + t * (int64_t)H, H, row, row + H)",
                                      "quantize_row(x + t * (int64_t)H, H, row, row + H + 1)"),
     "bf16_ties_away_from_zero": ("double r = nearbyint(a / q) * q;", "double r = round(a / q) * q;"),
