@@ -52,6 +52,8 @@ PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = {
     "combine_kernel": "combine_route_topk_amd/csrc/combine.hip",
     "permute_kernel": "combine_route_topk_amd/csrc/permute.hip",
+    "permute_fp8_kernel": "combine_route_topk_amd/csrc/fp8.hip",
+    "regroup_rows_kernel": "combine_route_topk_amd/csrc/regroup.hip",
 }
 
 
@@ -116,7 +118,7 @@ def stored_traffic(kernel, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
-def bench_regroup(moe, torch, lay, send, S, El, H, rows, stream, warmup, steps):
+def bench_regroup(moe, torch, lay, send, S, El, H, rows, stream, warmup, steps, workload):
     """Receive-side regroup on this GPU's share: the send buffer read as a
     receive buffer of S source segments with El local experts each (counts =
     the layout's expert counts), regrouped expert-major and back. Per-call
@@ -181,13 +183,15 @@ def bench_regroup(moe, torch, lay, send, S, El, H, rows, stream, warmup, steps):
            "per_call_GBps": {n: round(v, 1) for n, v in gbps.items()},
            "roofline": {"bound": "hbm", "kernel": "regroup_rows_kernel", "achieved": round(gbps["regroup"], 1),
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                        "frac": round(gbps["regroup"] / HBM_PEAK_GBPS, 4), "algorithmic_bytes": nb["regroup"]}}
+                        "frac": round(gbps["regroup"] / HBM_PEAK_GBPS, 4),
+                        "traffic": stored_traffic("regroup_rows_kernel", workload),
+                        "algorithmic_bytes": nb["regroup"]}}
     log("regroup", out)
     return out
 
 
 def bench_fp8(moe, torch, calls, lay, x, wt, sh, res, T, H, E, k, send_rows, nbytes, stream,
-              warmup, steps):
+              warmup, steps, workload):
     """The step with the FP8 dispatch payload: route -> layout ->
     moe_dispatch_permute_fp8 -> combine. The expert is the identity on the
     decoded rows: y = moe_fp8_dequant(send) is made once, before timing (a
@@ -248,6 +252,7 @@ def bench_fp8(moe, torch, calls, lay, x, wt, sh, res, T, H, E, k, send_rows, nby
            "per_call_us": {n: round(v, 2) for n, v in us.items()},
            "roofline": {"bound": "hbm", "kernel": "permute_fp8_kernel", "achieved": round(gbps_p, 1),
                         "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(gbps_p / HBM_PEAK_GBPS, 4),
+                        "traffic": stored_traffic("permute_fp8_kernel", workload),
                         "algorithmic_bytes": nb["permute_fp8"]},
            "note": "send rows hold E4M3 codes plus one scale byte per 32 values; combine reads the "
                    "identity expert's bf16 output, decoded once before timing"}
@@ -398,9 +403,9 @@ def main():
 
     fp8 = None if args.no_fp8 or H % 32 else bench_fp8(
         moe, torch, calls, lay, x, wt, sh, res, T, H, E, k, send_rows, nbytes, stream,
-        args.warmup, args.steps)
+        args.warmup, args.steps, w.name)
     regroup = None if args.no_regroup or R < 2 else bench_regroup(
-        moe, torch, lay, send, R, E // R, H, send_rows, stream, args.warmup, args.steps)
+        moe, torch, lay, send, R, E // R, H, send_rows, stream, args.warmup, args.steps, w.name)
 
     copy_probe = None
     if args.copy_probe_mib:
