@@ -68,11 +68,12 @@ def _load():
         lib.oracle_fp8_quantize_rows.argtypes = [P, i64, i32, P, P]
         lib.oracle_fp8_dequant_rows.argtypes = [P, P, i64, i32, P]
         lib.oracle_dispatch_permute_fp8.argtypes = [P, P, i64, i32, i32, P, i64, i64]
+        lib.oracle_expert_linear.argtypes = [P, P, i32, i32, i32, i32, P, P]
         for f in ("oracle_route_topk", "oracle_route_topk_grouped", "oracle_dispatch_layout",
                   "oracle_dispatch_permute", "oracle_combine_reduce", "oracle_recv_regroup_layout",
                   "oracle_scatter_rows", "oracle_gather_rows", "oracle_e4m3_round",
                   "oracle_fp8_block_exponent", "oracle_fp8_quantize_rows", "oracle_fp8_dequant_rows",
-                  "oracle_dispatch_permute_fp8"):
+                  "oracle_dispatch_permute_fp8", "oracle_expert_linear"):
             getattr(lib, f).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -301,3 +302,24 @@ def dispatch_permute_fp8(x: np.ndarray, pos: np.ndarray, send_rows: int, row_byt
     if _load().oracle_dispatch_permute_fp8(_ptr(x), _ptr(pos), T, H, k, _ptr(send), send_rows, rb) != 0:
         raise ValueError("oracle_dispatch_permute_fp8 rejected its arguments")
     return send
+
+
+# ---------------------------------------------------------------------------
+# tile-signalled return: stand-in expert computation
+# ---------------------------------------------------------------------------
+
+def expert_linear(recv: np.ndarray, cnt: np.ndarray, W: np.ndarray) -> np.ndarray:
+    """y [N, H_out] bf16 bits: each received row times its local expert's
+    W[l] ([H_out, H]), summed in float64 and rounded once to bf16."""
+    recv = _c(recv, np.uint16)
+    cnt = _c(cnt, np.int32)
+    W = _c(W, np.uint16)
+    S, El = cnt.shape
+    N = int(cnt.sum())
+    H = recv.shape[1]
+    H_out = W.shape[1]
+    assert W.shape == (El, H_out, H) and recv.shape[0] >= N
+    y = np.empty((N, H_out), np.uint16)
+    if _load().oracle_expert_linear(_ptr(recv), _ptr(cnt), S, El, H, H_out, _ptr(W), _ptr(y)) != 0:
+        raise ValueError("oracle_expert_linear rejected its arguments")
+    return y

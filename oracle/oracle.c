@@ -692,3 +692,52 @@ int oracle_dispatch_permute_fp8(const uint16_t *x, const int32_t *pos, int64_t T
     }
     return 0;
 }
+
+/* ------------------------------------------------------------------ */
+/* tile-signalled return: stand-in expert computation                  */
+/* ------------------------------------------------------------------ */
+
+/*
+ * The overlap the pages describe needs an expert matmul whose output tiles
+ * each belong to one return destination: a grouped GEMM over the
+ * (source, local expert) blocks of the receive buffer, so every tile's rows
+ * go back to one source as one contiguous write (thecoregrid
+ * "Mixture-of-experts acceleration through overlap": a producer GEMM with
+ * per-tile readiness flags, a consumer that starts each transfer when its
+ * tiles are ready, the remote-owner-aligned layout; aicassindra
+ * "gpu_moe_all_to_all", "Overlapping dispatch with expert compute": the
+ * strict chain dispatch -> compute -> combine).
+ *
+ * The stand-in expert is one linear map per local expert, W[l] of shape
+ * [H_out][H] (output-major). For every received row i, held in block
+ * (s, l) of the source-major receive buffer (cnt[s][l] rows of local
+ * expert l from source s, sources in order, experts in order inside each):
+ *   y[i][o] = sum_h recv[i][h] * W[l][o][h]
+ * in double precision, rounded once to bf16 (nearest, ties to even). The
+ * return is a bit copy of y's rows to the same positions of the sources'
+ * return buffers, which on one device is y itself.
+ * Returns 0, or -1 on bad sizes or negative counts.
+ */
+int oracle_expert_linear(const uint16_t *recv, const int32_t *cnt, int32_t S, int32_t E_l,
+                         int32_t H, int32_t H_out, const uint16_t *W, uint16_t *y)
+{
+    if (S <= 0 || E_l <= 0 || H <= 0 || H_out <= 0)
+        return -1;
+    for (int32_t i = 0; i < S * E_l; ++i)
+        if (cnt[i] < 0)
+            return -1;
+    int64_t row = 0;
+    for (int32_t s = 0; s < S; ++s)
+        for (int32_t l = 0; l < E_l; ++l)
+            for (int32_t r = 0; r < cnt[s * E_l + l]; ++r, ++row) {
+                const uint16_t *xr = recv + row * H;
+                const uint16_t *wl = W + (int64_t)l * H_out * H;
+                for (int32_t o = 0; o < H_out; ++o) {
+                    double acc = 0.0;
+                    for (int32_t h = 0; h < H; ++h)
+                        acc += bf16_value(xr[h]) * bf16_value(wl[(int64_t)o * H + h]);
+                    y[row * H_out + o] = oracle_bf16_round(acc);
+                }
+            }
+    return 0;
+}

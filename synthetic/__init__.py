@@ -21,7 +21,7 @@ Workload shapes follow the regimes the pages describe:
 
 Random streams: one numpy PCG64 generator per tensor, seeded with
 SeedSequence([seed, stream]) where stream is 0 logits, 1 bias, 2 x,
-3 residual, 4 shared. bf16 tensors are drawn as float32 normals and rounded
+3 residual, 4 shared, 5 the stand-in expert weights. bf16 tensors are drawn as float32 normals and rounded
 to bf16 by torch's CPU conversion; they are returned as uint16 bit patterns.
 """
 
@@ -38,6 +38,7 @@ STREAM_BIAS = 1
 STREAM_X = 2
 STREAM_RESIDUAL = 3
 STREAM_SHARED = 4
+STREAM_EXPERT_W = 5
 
 
 @dataclasses.dataclass(frozen=True)
@@ -145,6 +146,14 @@ def make_inputs(w: Workload, seed: int = 0, with_activations: bool = True) -> di
         d["residual"] = normal_bf16(seed, STREAM_RESIDUAL, (w.T, w.H)) if w.residual else None
         d["shared"] = normal_bf16(seed, STREAM_SHARED, (w.T, w.H)) if w.shared else None
     return d
+
+
+def make_expert_weights(E_l: int, H_out: int, H: int, seed: int = 0) -> np.ndarray:
+    """Stand-in expert weights [E_l][H_out][H] (one linear map per local
+    expert, output-major like a linear layer's weight), float32 normals
+    scaled by 1/sqrt(H) so outputs keep unit scale, as bf16 bits."""
+    w = rng(seed, STREAM_EXPERT_W).standard_normal((E_l, H_out, H), dtype=np.float32)
+    return bf16_bits_from_f32(w * np.float32(1.0 / math.sqrt(H)))
 
 
 def round_robin_idx(T: int, E: int, k: int) -> np.ndarray:

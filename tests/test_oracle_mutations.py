@@ -14,7 +14,7 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PIN_TESTS = ["tests/test_oracle_route.py", "tests/test_oracle_layout.py", "tests/test_oracle_combine.py",
-             "tests/test_oracle_regroup.py", "tests/test_oracle_fp8.py"]
+             "tests/test_oracle_regroup.py", "tests/test_oracle_fp8.py", "tests/test_oracle_expert.py"]
 
 MUTATIONS = {
     "tie_break_to_higher_id": ("    return ia < ib;\n", "    return ia > ib;\n"),
@@ -54,6 +54,12 @@ MUTATIONS = {
                                         "            for (int64_t b = H + H / 32 + 1; b < row_bytes; ++b)\n                row[b] = 0;"),
     "fp8_permute_scales_misplaced": ("quantize_row(x + t * (int64_t)H, H, row, row + H)",
                                      "quantize_row(x + t * (int64_t)H, H, row, row + H + 1)"),
+    "expert_weights_of_next_expert": ("const uint16_t *wl = W + (int64_t)l * H_out * H;",
+                                      "const uint16_t *wl = W + (int64_t)((l + 1) % E_l) * H_out * H;"),
+    "expert_weights_transposed": ("acc += bf16_value(xr[h]) * bf16_value(wl[(int64_t)o * H + h]);",
+                                  "acc += bf16_value(xr[h]) * bf16_value(wl[(int64_t)h * H_out + o]);"),
+    "expert_drops_last_term": ("                    for (int32_t h = 0; h < H; ++h)\n                        acc +=",
+                               "                    for (int32_t h = 0; h < H - 1; ++h)\n                        acc +="),
     "bf16_ties_away_from_zero": ("double r = nearbyint(a / q) * q;", "double r = round(a / q) * q;"),
     "bf16_no_subnormal_spacing": ("if (e < -126)\n        e = -126;", "if (e < -140)\n        e = -140;"),
 }
