@@ -20,11 +20,14 @@ for kept rows only:
 with N kept rows and T_read tokens that have at least one kept replica (both
 read from the path's own outputs after the timed region).
 
-After the path, two further measurements are reported under "next_rows",
-neither part of `value`: the same step with the FP8 dispatch payload
-(moe_dispatch_permute_fp8 in place of the bf16 permute), and the
-receive-side regroup on the same buffers (the send buffer read as R source
-segments).
+After the path, three further measurements are reported under "next_rows",
+none part of `value`:
+  * the same step with the FP8 dispatch payload (moe_dispatch_permute_fp8 in
+    place of the bf16 permute);
+  * the receive-side regroup on the same buffers (the send buffer read as R
+    source segments);
+  * the tile-signalled return: a stand-in expert GEMM on those segments whose
+    tiles are returned as they finish, against the GEMM then a copy.
 
 The CPU-baseline leg times the plain C oracle on the same host arrays.
 """
@@ -71,6 +74,8 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-fp8", action="store_true",
                    help="skip the FP8-payload step measurement (reported under next_rows)")
+    p.add_argument("--no-tile-return", action="store_true",
+                   help="skip the tile-signalled return measurement (reported under next_rows)")
     p.add_argument("--no-regroup", action="store_true",
                    help="skip the receive-side regroup measurement (reported under next_rows)")
     p.add_argument("--cpu-seconds", type=float, default=10.0,
@@ -260,6 +265,64 @@ def bench_fp8(moe, torch, calls, lay, x, wt, sh, res, T, H, E, k, send_rows, nby
     return report
 
 
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_tile_return(moe, torch, lay, send, S, El, H, rows, stream, warmup, steps, seed=0):
+    """Tile-signalled return on this GPU's share: the send buffer read as S
+    source segments of El local experts goes through a stand-in expert (one
+    H x H linear map per local expert, MFMA bf16), and the results return to
+    the sources' buffer. Timed: the GEMM alone, the GEMM then a copy of y to
+    ret (the return starting after the GEMM), and the signalled launch with
+    32 dedicated consumer blocks and with none (producers return their own
+    tasks). FLOPs per GEMM: 2 * N * H * H."""
+    dev = send.device
+    cnt = lay["expert_counts"].view(S, El)
+    W = torch.from_numpy(synthetic.make_expert_weights(El, H, H, seed).view(np.int16)).to(dev).view(torch.bfloat16)
+    ws = torch.empty(moe.moe_expert_linear_workspace_size(S, El, rows), dtype=torch.uint8, device=dev)
+    y = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+    ret = torch.empty_like(y)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps * 1e3
+
+    gemm = lambda: moe.moe_expert_linear(send, cnt, W, y=y, workspace=ws)
+    us = {"gemm": timed(gemm), "gemm_then_copy": timed(lambda: (gemm(), ret.copy_(y)))}
+    status = {}
+    for consumers in (32, 0):
+        key = f"signalled_consumers_{consumers}"
+        us[key] = timed(lambda: moe.moe_expert_linear_return(send, cnt, W, 0, consumers, 2, y=y, ret=ret,
+                                                             workspace=ws))
+        status[key] = int(ws[:4].view(torch.int32).item())
+    if any(status.values()):
+        raise RuntimeError(f"tile-signalled return reported status {status}")
+    N = int(lay["expert_offsets"][-1].item())
+    if not torch.equal(ret[:N].view(torch.int16), y[:N].view(torch.int16)):
+        raise RuntimeError("returned rows differ from the expert output")
+    flops = 2.0 * N * H * H
+    tflops = flops / (us["gemm"] * 1e-6) / 1e12
+    best = min(("signalled_consumers_32", "signalled_consumers_0"), key=lambda k: us[k])
+    out = {"rows": N, "sources": S, "local_experts": El, "H": H,
+           "per_call_us": {k: round(v, 1) for k, v in us.items()},
+           "signalled_vs_sequential": round(us["gemm_then_copy"] / us[best], 3),
+           "best_signalled": best,
+           "roofline": {"bound": "mfma", "kernel": "expert_linear_kernel", "achieved": round(tflops, 1),
+                        "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                        "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "flops": flops},
+           "note": "stand-in expert: one bf16 H x H linear map per local expert; band_group 2"}
+    log("tile-signalled return", out)
+    return out
+
+
 def cpu_baseline(w, d, budget_s):
     """Time the single-threaded C oracle over the same workload."""
     import oracle
@@ -404,6 +467,8 @@ def main():
     fp8 = None if args.no_fp8 or H % 32 else bench_fp8(
         moe, torch, calls, lay, x, wt, sh, res, T, H, E, k, send_rows, nbytes, stream,
         args.warmup, args.steps, w.name)
+    tile_return = None if args.no_tile_return or R < 2 or H % 128 else bench_tile_return(
+        moe, torch, lay, send, R, E // R, H, send_rows, stream, args.warmup, args.steps)
     regroup = None if args.no_regroup or R < 2 else bench_regroup(
         moe, torch, lay, send, R, E // R, H, send_rows, stream, args.warmup, args.steps, w.name)
 
@@ -455,6 +520,8 @@ def main():
         next_rows["fp8_dispatch"] = fp8
     if regroup:
         next_rows["recv_regroup"] = regroup
+    if tile_return:
+        next_rows["tile_signalled_return"] = tile_return
     if next_rows:
         result["next_rows"] = next_rows
     if copy_probe:

@@ -31,7 +31,9 @@ MOE_COMBINE_OUT_FP32 = 1
 EXPORTS = ("moe_route_topk", "moe_route_topk_grouped", "moe_layout_workspace_size", "moe_dispatch_layout",
            "moe_dispatch_permute", "moe_combine_reduce", "moe_fp8_row_bytes",
            "moe_dispatch_permute_fp8", "moe_fp8_dequant", "moe_recv_regroup_workspace_size",
-           "moe_recv_regroup_layout", "moe_recv_regroup", "moe_recv_ungroup", "moe_status_string")
+           "moe_recv_regroup_layout", "moe_recv_regroup", "moe_recv_ungroup",
+           "moe_expert_linear_workspace_size", "moe_expert_linear", "moe_expert_linear_return",
+           "moe_expert_return_slots", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -61,6 +63,11 @@ def _load_library() -> ctypes.CDLL:
     lib.moe_recv_regroup_layout.argtypes = [P, i32, i32, P, P, P, i64, P, ctypes.c_size_t, P]
     lib.moe_recv_regroup.argtypes = [P, P, P, i64, i32, P, P]
     lib.moe_recv_ungroup.argtypes = [P, P, P, i64, i32, P, P]
+    lib.moe_expert_linear_workspace_size.argtypes = [i32, i32, i64, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_expert_linear.argtypes = [P, P, i32, i32, i32, i32, P, i64, P, P, ctypes.c_size_t, P]
+    lib.moe_expert_linear_return.argtypes = [P, P, i32, i32, i32, i32, P, i64, i32, i32, i32, P, P, P,
+                                             ctypes.c_size_t, P]
+    lib.moe_expert_return_slots.argtypes = [ctypes.POINTER(ctypes.c_int32)]
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     for name in EXPORTS[:-1]:
@@ -303,3 +310,60 @@ def moe_fp8_dequant(rows: torch.Tensor, H: int, n_rows: Optional[torch.Tensor] =
         _ptr(rows, (torch.uint8,), "rows", 2), None if n_rows is None else _ptr(n_rows, _I32, "n_rows"),
         max_rows, H, _ptr(out, _BF16, "out", 2), _stream(stream)))
     return out
+
+
+def moe_expert_linear_workspace_size(S: int, E_l: int, max_rows: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_expert_linear_workspace_size", lib.moe_expert_linear_workspace_size(S, E_l, max_rows, ctypes.byref(n)))
+    return n.value
+
+
+def moe_expert_return_slots() -> int:
+    n = ctypes.c_int32(0)
+    _check("moe_expert_return_slots", lib.moe_expert_return_slots(ctypes.byref(n)))
+    return n.value
+
+
+def _linear_args(recv, recv_counts, W, y, workspace):
+    S, El = recv_counts.shape
+    max_rows, H = recv.shape
+    El_w, H_out, H_w = W.shape
+    if El_w != El or H_w != H:
+        raise ValueError(f"W must be [{El}, H_out, {H}], got {tuple(W.shape)}")
+    if y is None:
+        y = torch.empty((max_rows, H_out), dtype=torch.bfloat16, device=recv.device)
+    if workspace is None:
+        workspace = torch.empty(moe_expert_linear_workspace_size(S, El, max_rows), dtype=torch.uint8,
+                                device=recv.device)
+    return S, El, max_rows, H, H_out, y, workspace
+
+
+def moe_expert_linear(recv: torch.Tensor, recv_counts: torch.Tensor, W: torch.Tensor,
+                      y: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                      stream=None) -> torch.Tensor:
+    """y [max_rows, H_out] bf16: each received row times its local expert's
+    W[l]^T (see moe_expert_linear)."""
+    S, El, max_rows, H, H_out, y, workspace = _linear_args(recv, recv_counts, W, y, workspace)
+    _check("moe_expert_linear", lib.moe_expert_linear(
+        _ptr(recv, _BF16, "recv", 2), _ptr(recv_counts, _I32, "recv_counts", 2), S, El, H, H_out,
+        _ptr(W, _BF16, "W", 3), max_rows, _ptr(y, _BF16, "y", 2),
+        _ptr(workspace, (torch.uint8,), "workspace"), workspace.numel(), _stream(stream)))
+    return y
+
+
+def moe_expert_linear_return(recv: torch.Tensor, recv_counts: torch.Tensor, W: torch.Tensor,
+                             self_rank: int, consumer_blocks: int, band_group: int,
+                             y: Optional[torch.Tensor] = None, ret: Optional[torch.Tensor] = None,
+                             workspace: Optional[torch.Tensor] = None, stream=None):
+    """(y, ret, workspace): the expert output and the rows returned to their
+    sources, produced tile by tile with per-band flags (see
+    moe_expert_linear_return). workspace[:4] holds the status word."""
+    S, El, max_rows, H, H_out, y, workspace = _linear_args(recv, recv_counts, W, y, workspace)
+    if ret is None:
+        ret = torch.empty((max_rows, H_out), dtype=torch.bfloat16, device=recv.device)
+    _check("moe_expert_linear_return", lib.moe_expert_linear_return(
+        _ptr(recv, _BF16, "recv", 2), _ptr(recv_counts, _I32, "recv_counts", 2), S, El, H, H_out,
+        _ptr(W, _BF16, "W", 3), max_rows, self_rank, consumer_blocks, band_group,
+        _ptr(y, _BF16, "y", 2), _ptr(ret, _BF16, "ret", 2),
+        _ptr(workspace, (torch.uint8,), "workspace"), workspace.numel(), _stream(stream)))
+    return y, ret, workspace

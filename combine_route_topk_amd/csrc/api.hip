@@ -331,6 +331,98 @@ moe_status_t moe_recv_ungroup(const uint16_t *grouped, const int32_t *recv_pos,
     return regroup_rows(grouped, recv_pos, n_rows, max_rows, H, true, out, stream);
 }
 
+namespace {
+
+moe_status_t check_linear(const uint16_t *recv, const int32_t *cnt, int32_t S, int32_t El,
+                          int32_t H, int32_t H_out, const uint16_t *W, int64_t max_rows,
+                          const void *y, const void *workspace, size_t workspace_bytes)
+{
+    moe_status_t s = check_regroup_sizes(S, El);
+    if (s != MOE_OK)
+        return s;
+    if (max_rows < 0)
+        return MOE_ERR_INVALID_ARG;
+    if (max_rows >= kMaxAssignments)
+        return MOE_ERR_UNSUPPORTED;
+    if (H <= 0 || H % 64 != 0 || H > kMaxH || H_out <= 0 || H_out % 128 != 0 || H_out > kMaxH)
+        return MOE_ERR_UNSUPPORTED;
+    if (!cnt || (max_rows > 0 && (!recv || !W || !y)))
+        return MOE_ERR_INVALID_ARG;
+    if (!aligned(cnt, 4) || !aligned(recv, 16) || !aligned(W, 16) || !aligned(y, 16))
+        return MOE_ERR_INVALID_ARG;
+    if (!workspace || workspace_bytes < moe::expert_linear_workspace_bytes(S, El, max_rows) ||
+        !aligned(workspace, 16))
+        return MOE_ERR_WORKSPACE;
+    return MOE_OK;
+}
+
+}  // namespace
+
+moe_status_t moe_expert_linear_workspace_size(int32_t S, int32_t E_l, int64_t max_rows,
+                                              size_t *bytes)
+{
+    if (!bytes || max_rows < 0)
+        return MOE_ERR_INVALID_ARG;
+    moe_status_t s = check_regroup_sizes(S, E_l);
+    if (s != MOE_OK)
+        return s;
+    if (max_rows >= kMaxAssignments)
+        return MOE_ERR_UNSUPPORTED;
+    *bytes = moe::expert_linear_workspace_bytes(S, E_l, max_rows);
+    return MOE_OK;
+}
+
+moe_status_t moe_expert_linear(const uint16_t *recv, const int32_t *recv_counts, int32_t S,
+                               int32_t E_l, int32_t H, int32_t H_out, const uint16_t *W,
+                               int64_t max_rows, uint16_t *y, void *workspace,
+                               size_t workspace_bytes, void *stream)
+{
+    moe_status_t s = check_linear(recv, recv_counts, S, E_l, H, H_out, W, max_rows, y, workspace,
+                                  workspace_bytes);
+    if (s != MOE_OK)
+        return s;
+    return from_hip(moe::launch_expert_linear(recv, recv_counts, S, E_l, H, H_out, W, max_rows, y,
+                                              static_cast<int32_t *>(workspace),
+                                              static_cast<hipStream_t>(stream)));
+}
+
+moe_status_t moe_expert_linear_return(const uint16_t *recv, const int32_t *recv_counts,
+                                      int32_t S, int32_t E_l, int32_t H, int32_t H_out,
+                                      const uint16_t *W, int64_t max_rows, int32_t self_rank,
+                                      int32_t consumer_blocks, int32_t band_group, uint16_t *y,
+                                      uint16_t *ret, void *workspace, size_t workspace_bytes,
+                                      void *stream)
+{
+    moe_status_t s = check_linear(recv, recv_counts, S, E_l, H, H_out, W, max_rows, y, workspace,
+                                  workspace_bytes);
+    if (s != MOE_OK)
+        return s;
+    if (self_rank < 0 || self_rank >= S || consumer_blocks < 0 || band_group < 1)
+        return MOE_ERR_INVALID_ARG;
+    if (max_rows > 0 && (!ret || !aligned(ret, 16)))
+        return MOE_ERR_INVALID_ARG;
+    int slots = 0;
+    if (moe::expert_return_slots(&slots) != hipSuccess)
+        return MOE_ERR_LAUNCH;
+    if (consumer_blocks >= slots)
+        return MOE_ERR_UNSUPPORTED;
+    int32_t grid = 0;
+    return from_hip(moe::launch_expert_return(
+        recv, recv_counts, S, E_l, H, H_out, W, max_rows, self_rank, consumer_blocks, band_group,
+        y, ret, static_cast<int32_t *>(workspace), static_cast<hipStream_t>(stream), &grid));
+}
+
+moe_status_t moe_expert_return_slots(int32_t *slots)
+{
+    if (!slots)
+        return MOE_ERR_INVALID_ARG;
+    int n = 0;
+    if (moe::expert_return_slots(&n) != hipSuccess)
+        return MOE_ERR_LAUNCH;
+    *slots = n;
+    return MOE_OK;
+}
+
 const char *moe_status_string(moe_status_t status)
 {
     switch (status) {

@@ -1,0 +1,580 @@
+// expert.hip -- tile-signalled return path: a stand-in expert GEMM over the
+// (source, local expert) blocks of a receive buffer, whose output tiles
+// publish readiness flags, and a consumer that returns each source's rows
+// as soon as they are ready.
+//
+// Method: thecoregrid "Mixture-of-experts acceleration through overlap"
+// (producer GEMM and consumer kept apart but synchronised per tile: the
+// GEMM epilogue publishes a flag per tile; the consumer starts a transfer
+// once enough row bands are ready and moves several bands per transfer;
+// tiles are tied to one destination, remote-owner-aligned, and remote
+// tiles are computed first; the GPU's compute units are split between the
+// two roles); aicassindra "gpu_moe_all_to_all", "Overlapping dispatch with
+// expert compute" (the strict dispatch -> compute -> combine chain that
+// per-tile signalling relaxes).
+//
+// On one GPU the R sources are partitions of one buffer, so the "transfer"
+// is a copy of a contiguous row range from the expert output y to the
+// return buffer ret, which has the same layout as the sources' send
+// buffers: combine then reads ret unchanged.
+//
+// Kernels:
+//  * linear_table_kernel (one block): from the S x E_l counts, the first row
+//    of every (source, expert) block, the row bands (128-row tiles of a
+//    block) counted in remote-first order -- sources self+1, self+2, ...,
+//    self last -- and the consumer tasks (up to band_group bands of one
+//    source). It also clears the band flags and the status word, with
+//    ordinary stores, so a call needs no memset.
+//  * expert_linear_kernel: a persistent grouped GEMM. Tile = 128 rows x 128
+//    output columns of one band, K-steps of 64; 256 threads as 2 x 2 waves,
+//    each wave 64 x 64 with v_mfma_f32_32x32x16_bf16 (bf16 in, fp32
+//    accumulate). The next K-step's tiles are prefetched into registers
+//    while the current one is multiplied from LDS (rows padded to 144 bytes,
+//    conflict-free 16-byte fragment reads). The epilogue rounds to bf16
+//    (nearest even), stages the tile in LDS and writes 16-byte row chunks.
+//    Tiles are dealt so that each XCD takes runs of consecutive tiles: a
+//    band's 128-row A slab is read into one L2.
+//  * expert_return_kernel: the same GEMM in producer blocks, which after
+//    each tile release-add 1 to the band's counter; consumer blocks take
+//    tasks in order, wait (bounded) until every band of the task counts
+//    all its column tiles, then copy the task's rows to ret. One cooperative
+//    launch keeps every block resident, so no consumer waits on a producer
+//    that cannot run; a wait that exceeds its bound sets the status word
+//    and skips the copy instead of spinning on.
+#include <hip/hip_cooperative_groups.h>
+
+#include "device.hpp"
+#include "launch.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBM = 128, kBN = 128, kBK = 64;
+constexpr int kRowBytes = kBK * 2 + 16;        // LDS row: 64 bf16 + 16 bytes of padding
+constexpr int kTileLds = kBM * kRowBytes;      // one operand tile in LDS
+constexpr int kCRowBytes = kBN * 2 + 16;       // LDS row of the staged output tile
+constexpr int kLdsBytes = 2 * kTileLds;        // A and B tiles (the output stage fits inside)
+static_assert(kBM * kCRowBytes <= kLdsBytes, "output stage must fit the operand space");
+constexpr int kTableThreads = 1024;
+constexpr int kColGroup = 4;                  // column tiles per producer work unit
+constexpr int kSpinLimit = 1 << 21;            // polls before a wait gives up (about 1 s)
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Workspace layout (int32 words), for SE = S * E_l blocks and NBmax bands.
+struct LinearWs {
+    int32_t *status;       // [1]      0; 1 = a consumer wait expired; 2 = counts exceed the buffers
+    int32_t *counts;       // [2]      total bands, total consumer tasks
+    int32_t *blk_row;      // [SE]     first row of source-major block s*E_l+l
+    int32_t *band_prefix;  // [SE + 1] bands before remote-first block q*E_l+l
+    int32_t *task_prefix;  // [S + 1]  consumer tasks before remote-first source q
+    int32_t *flags;        // [NBmax]  finished column tiles per band
+    int32_t *task_flags;   // [NBmax]  finished bands per consumer task (inline return)
+};
+
+__host__ __device__ inline int64_t max_bands(int32_t S, int32_t El, int64_t max_rows)
+{
+    return (int64_t)S * El + (max_rows + kBM - 1) / kBM;
+}
+
+// the flag arrays' length is kept in the workspace itself (word 3)
+__host__ __device__ inline int64_t max_bands_of(const int32_t *base) { return base[3]; }
+
+__host__ __device__ inline LinearWs linear_ws(int32_t *base, int32_t S, int32_t El)
+{
+    const int64_t SE = (int64_t)S * El;
+    LinearWs w;
+    w.status = base;
+    w.counts = base + 1;
+    w.blk_row = base + 4;
+    w.band_prefix = w.blk_row + SE;
+    w.task_prefix = w.band_prefix + SE + 1;
+    w.flags = w.task_prefix + S + 1;
+    w.task_flags = w.flags + max_bands_of(base);
+    return w;
+}
+
+__host__ __device__ inline int64_t linear_ws_words(int32_t S, int32_t El, int64_t max_rows)
+{
+    return 4 + 2 * (int64_t)S * El + 1 + S + 1 + 2 * max_bands(S, El, max_rows);
+}
+
+// exclusive scan of one value per thread over a 1024-thread block
+__device__ int32_t block_scan(int32_t v, int32_t *wave_total, int32_t *total)
+{
+    constexpr int WAVES = kTableThreads / kWave;
+    const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+    const int32_t inc = wave_inclusive_sum(v);
+    __syncthreads();
+    if (lane == kWave - 1)
+        wave_total[w] = inc;
+    __syncthreads();
+    int32_t before = 0, all = 0;
+#pragma unroll
+    for (int u = 0; u < WAVES; ++u) {
+        before += u < w ? wave_total[u] : 0;
+        all += wave_total[u];
+    }
+    *total = all;
+    return before + inc - v;
+}
+
+// Each thread owns up to 4 consecutive entries of a 4096-entry sequence.
+__global__ __launch_bounds__(kTableThreads) void linear_table_kernel(
+    const int32_t *__restrict__ cnt, int32_t S, int32_t El, int32_t self_rank, int32_t band_group,
+    int64_t max_rows, int64_t flag_words, int32_t *__restrict__ ws_base)
+{
+    __shared__ int32_t wave_total[kTableThreads / kWave];
+    __shared__ unsigned long long rows64;  // the row total without int32 wrap-around
+    const int SE = S * El;
+    const int tid = threadIdx.x;
+    if (tid == 0) {
+        rows64 = 0;
+        ws_base[3] = (int32_t)flag_words;
+    }
+    __syncthreads();
+    const LinearWs ws = linear_ws(ws_base, S, El);
+    for (int64_t i = tid; i < 2 * flag_words; i += kTableThreads)
+        ws.flags[i] = 0;  // band counts, then task counts
+    // 1) first rows of the source-major blocks
+    int32_t c[4], part = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int b = tid * 4 + u;
+        c[u] = b < SE ? max(cnt[b], 0) : 0;
+        part += c[u];
+    }
+    __syncthreads();
+    atomicAdd(&rows64, (unsigned long long)c[0] + c[1] + c[2] + c[3]);
+    int32_t total;
+    int32_t run = block_scan(part, wave_total, &total);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int b = tid * 4 + u;
+        if (b < SE)
+            ws.blk_row[b] = run;
+        run += c[u];
+    }
+    // 2) bands in remote-first order: block rb = q*El + l is source (self+1+q) % S
+    int32_t nb[4];
+    part = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int rb = tid * 4 + u;
+        nb[u] = 0;
+        if (rb < SE) {
+            const int q = rb / El, l = rb - q * El;
+            const int s = (self_rank + 1 + q) % S;
+            nb[u] = (int32_t)(((int64_t)max(cnt[s * El + l], 0) + kBM - 1) / kBM);
+        }
+        part += nb[u];
+    }
+    int32_t n_bands;
+    run = block_scan(part, wave_total, &n_bands);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const int rb = tid * 4 + u;
+        if (rb < SE)
+            ws.band_prefix[rb] = run;
+        run += nb[u];
+    }
+    // 3) consumer tasks per remote-first source q: ceil(bands of q / band_group)
+    int32_t tasks = 0;
+    if (tid < S) {
+        int32_t bq = 0;
+        for (int l = 0; l < El; ++l) {
+            const int s = (self_rank + 1 + tid) % S;
+            bq += (int32_t)(((int64_t)max(cnt[s * El + l], 0) + kBM - 1) / kBM);
+        }
+        tasks = (bq + band_group - 1) / band_group;
+    }
+    int32_t n_tasks;
+    const int32_t tstart = block_scan(tasks, wave_total, &n_tasks);
+    if (tid < S)
+        ws.task_prefix[tid] = tstart;
+    if (tid == 0) {
+        // counts totalling more rows than the buffers hold: publish no work
+        const bool fits = rows64 <= (unsigned long long)max_rows;
+        ws.band_prefix[SE] = n_bands;
+        ws.task_prefix[S] = n_tasks;
+        ws.counts[0] = fits ? n_bands : 0;
+        ws.counts[1] = fits ? n_tasks : 0;
+        ws.status[0] = fits ? 0 : 2;
+    }
+}
+
+// largest index i in [0, n) with a[i] <= v (a ascending, a[0] <= v)
+__device__ __forceinline__ int upper_index(const int32_t *a, int n, int32_t v)
+{
+    int lo = 0, hi = n - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (a[mid] <= v)
+            lo = mid;
+        else
+            hi = mid - 1;
+    }
+    return lo;
+}
+
+struct Band {
+    int32_t row0;   // first row of the band
+    int32_t rows;   // rows in the band (1..128)
+    int32_t l;      // local expert
+};
+
+// band index (remote-first order) -> rows and expert
+__device__ __forceinline__ Band band_info(const LinearWs &ws, const int32_t *cnt, int32_t S,
+                                          int32_t El, int32_t self_rank, int32_t band)
+{
+    const int SE = S * El;
+    const int rb = upper_index(ws.band_prefix, SE, band);
+    const int q = rb / El, l = rb - q * El;
+    const int s = (self_rank + 1 + q) % S;
+    const int32_t rt = band - ws.band_prefix[rb];
+    const int32_t n = max(cnt[s * El + l], 0);
+    Band b;
+    b.row0 = ws.blk_row[s * El + l] + rt * kBM;
+    b.rows = min(kBM, n - rt * kBM);
+    b.l = l;
+    return b;
+}
+
+// One 128 x 128 output tile: y[row0 .. row0+rows)[n0 .. n0+128) =
+// x[rows] . W[l][n0 .. n0+128)^T, accumulated over K = H in fp32.
+__device__ void gemm_tile(const uint16_t *__restrict__ x, const uint16_t *__restrict__ Wl,
+                          int32_t row0, int32_t rows, int32_t n0, int32_t H, int32_t H_out,
+                          uint16_t *__restrict__ y, uint8_t *lds)
+{
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    const int wm = wave >> 1, wn = wave & 1;
+    // global -> register mapping: 4 rows per thread, one 16-byte chunk of the K-step each
+    const int lrow = tid >> 3, lchunk = tid & 7;
+    u32x4 ra[4], rb[4];
+    auto load = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = lrow + 32 * i;
+            ra[i] = r < rows ? *reinterpret_cast<const u32x4 *>(x + (int64_t)(row0 + r) * H + k0 + lchunk * 8)
+                             : u32x4{0u, 0u, 0u, 0u};
+            rb[i] = *reinterpret_cast<const u32x4 *>(Wl + (int64_t)(n0 + r) * H + k0 + lchunk * 8);
+        }
+    };
+    uint8_t *As = lds, *Bs = lds + kTileLds;
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            acc[i][j] = f32x16{};
+    load(0);
+    for (int k0 = 0; k0 < H; k0 += kBK) {
+        __syncthreads();  // the previous step's fragment reads are done
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = lrow + 32 * i;
+            *reinterpret_cast<u32x4 *>(As + r * kRowBytes + lchunk * 16) = ra[i];
+            *reinterpret_cast<u32x4 *>(Bs + r * kRowBytes + lchunk * 16) = rb[i];
+        }
+        __syncthreads();
+        if (k0 + kBK < H)
+            load(k0 + kBK);  // in flight while this step multiplies
+#pragma unroll
+        for (int kk = 0; kk < kBK; kk += 16) {
+            const int koff = (kk + 8 * (lane >> 5)) * 2;
+            bf16x8 af[2], bfr[2];
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                af[i] = *reinterpret_cast<const bf16x8 *>(As + (wm * 64 + i * 32 + (lane & 31)) * kRowBytes + koff);
+                bfr[i] = *reinterpret_cast<const bf16x8 *>(Bs + (wn * 64 + i * 32 + (lane & 31)) * kRowBytes + koff);
+            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
+    }
+    // epilogue: round to bf16, stage the tile in LDS, write 16-byte chunks of rows
+    __syncthreads();
+    uint16_t *Cs = reinterpret_cast<uint16_t *>(lds);
+    constexpr int kCStride = kCRowBytes / 2;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; r += 2) {
+                // accumulator r holds row 8(r/4) + 4(lane/32) + r%4, column lane%32
+                const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+                const int col = wn * 64 + j * 32 + (lane & 31);
+                const uint32_t p = pack_bf16x2(acc[i][j][r], acc[i][j][r + 1]);
+                Cs[row * kCStride + col] = (uint16_t)(p & 0xFFFFu);
+                Cs[(row + 1) * kCStride + col] = (uint16_t)(p >> 16);
+            }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = (tid >> 4) + 16 * i, chunk = tid & 15;
+        if (r < rows)
+            *reinterpret_cast<u32x4 *>(y + (int64_t)(row0 + r) * H_out + n0 + chunk * 8) =
+                *reinterpret_cast<const u32x4 *>(lds + r * kCRowBytes + chunk * 16);
+    }
+    __syncthreads();  // the stage is free again before the next tile's loads land
+}
+
+// the bands [b0, b1) of one consumer task (remote-first source q)
+__device__ __forceinline__ void task_bands(const LinearWs &ws, int32_t S, int32_t El,
+                                           int32_t band_group, int32_t task, int32_t *b0,
+                                           int32_t *b1)
+{
+    const int q = upper_index(ws.task_prefix, S, task);
+    const int32_t q_band0 = ws.band_prefix[q * El], q_band1 = ws.band_prefix[(q + 1) * El];
+    *b0 = q_band0 + (task - ws.task_prefix[q]) * band_group;
+    *b1 = min(*b0 + band_group, q_band1);
+}
+
+// copy the rows of bands [b0, b1) -- consecutive rows of one source -- from y to ret
+__device__ void return_rows(const LinearWs &ws, const int32_t *cnt, int32_t S, int32_t El,
+                            int32_t self_rank, int32_t H_out, int32_t b0, int32_t b1,
+                            const uint16_t *__restrict__ y, uint16_t *__restrict__ ret)
+{
+    const int32_t C16 = H_out / 8;
+    const Band first = band_info(ws, cnt, S, El, self_rank, b0);
+    const Band last = band_info(ws, cnt, S, El, self_rank, b1 - 1);
+    const int64_t r0 = first.row0, r1 = (int64_t)last.row0 + last.rows;
+    const int64_t n16 = (r1 - r0) * C16;
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(y) + r0 * C16;
+    u32x4 *dst = reinterpret_cast<u32x4 *>(ret) + r0 * C16;
+    // whole chunks keep 8 loads in flight per thread (32 KiB per block): no
+    // per-load condition, which would make each load wait for the last
+    constexpr int kInFlight = 8;
+    constexpr int64_t kChunk = (int64_t)kThreads * kInFlight;
+    const int64_t full = n16 / kChunk * kChunk;
+    for (int64_t base = threadIdx.x; base < full; base += kChunk) {
+        u32x4 v[kInFlight];
+#pragma unroll
+        for (int u = 0; u < kInFlight; ++u)
+            v[u] = load_stream(src + base + u * kThreads);
+#pragma unroll
+        for (int u = 0; u < kInFlight; ++u)
+            store_stream(dst + base + u * kThreads, v[u]);
+    }
+    for (int64_t i = full + threadIdx.x; i < n16; i += kThreads)
+        store_stream(dst + i, load_stream(src + i));
+}
+
+// tile order: each XCD (blockIdx % 8) takes runs of consecutive tile ids
+__device__ __forceinline__ int64_t dealt_tile(int64_t step, int32_t slot, int32_t n_slots)
+{
+    const int32_t per_xcd = n_slots / 8;
+    if (per_xcd == 0 || n_slots % 8 != 0)
+        return step * n_slots + slot;
+    return step * n_slots + (int64_t)(slot % 8) * per_xcd + slot / 8;
+}
+
+// signal: release-add each unit's column tiles to its band's count.
+// inline_return: the unit that completes a band counts the band toward its
+// task, and the unit that completes a task's last band copies the task's
+// rows to ret itself (acquire-release counts; no block ever waits).
+__device__ void produce(const uint16_t *__restrict__ x, const int32_t *__restrict__ cnt,
+                        int32_t S, int32_t El, int32_t self_rank, int32_t H, int32_t H_out,
+                        const uint16_t *__restrict__ W, uint16_t *__restrict__ y,
+                        const LinearWs &ws, int32_t slot, int32_t n_slots, bool signal,
+                        bool inline_return, int32_t band_group, uint16_t *__restrict__ ret,
+                        int32_t *copy_task, uint8_t *lds)
+{
+    // a work unit is one band by up to kColGroup column tiles; it is released
+    // once (one L2 write-back per unit instead of per tile)
+    const int32_t nct = H_out / kBN;
+    const int32_t groups = (nct + kColGroup - 1) / kColGroup;
+    const int64_t n_units = (int64_t)ws.counts[0] * groups;
+    for (int64_t step = 0; step * n_slots < n_units; ++step) {
+        const int64_t u = dealt_tile(step, slot, n_slots);
+        if (u >= n_units)
+            continue;
+        const int32_t band = (int32_t)(u / groups), g = (int32_t)(u % groups);
+        const Band b = band_info(ws, cnt, S, El, self_rank, band);
+        const int32_t ct1 = min(nct, (g + 1) * kColGroup);
+        for (int32_t ct = g * kColGroup; ct < ct1; ++ct)
+            gemm_tile(x, W + (int64_t)b.l * H_out * H, b.row0, b.rows, ct * kBN, H, H_out, y, lds);
+        if (signal) {
+            // each thread's stores complete to its L2 (a workgroup-scope release is
+            // a wait, no cache maintenance); then one agent-scope release by thread 0
+            // writes the L2 back once for the whole unit before the count moves
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                const int32_t add = ct1 - g * kColGroup;
+                int32_t task = -1;
+                if (!inline_return) {
+                    __hip_atomic_fetch_add(ws.flags + band, add, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+                } else if (__hip_atomic_fetch_add(ws.flags + band, add, __ATOMIC_RELEASE,
+                                                  __HIP_MEMORY_SCOPE_AGENT) + add == nct) {
+                    // this unit completed the band (its add read the final count):
+                    // acquire the other units' releases, then count the band
+                    // toward its task. Only band completions pay for the acquire.
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                    const int rb = upper_index(ws.band_prefix, S * El, band);
+                    const int q = rb / El;
+                    const int32_t t = ws.task_prefix[q] + (band - ws.band_prefix[q * El]) / band_group;
+                    int32_t b0, b1;
+                    task_bands(ws, S, El, band_group, t, &b0, &b1);
+                    if (__hip_atomic_fetch_add(ws.task_flags + t, 1, __ATOMIC_ACQ_REL,
+                                               __HIP_MEMORY_SCOPE_AGENT) + 1 == b1 - b0)
+                        task = t;
+                }
+                *copy_task = task;
+            }
+            __syncthreads();
+            if (inline_return && *copy_task >= 0) {
+                int32_t b0, b1;
+                task_bands(ws, S, El, band_group, *copy_task, &b0, &b1);
+                return_rows(ws, cnt, S, El, self_rank, H_out, b0, b1, y, ret);
+            }
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads) void expert_linear_kernel(
+    const uint16_t *__restrict__ x, const int32_t *__restrict__ cnt, int32_t S, int32_t El,
+    int32_t self_rank, int32_t H, int32_t H_out, const uint16_t *__restrict__ W,
+    uint16_t *__restrict__ y, int32_t *__restrict__ ws_base)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+    const LinearWs ws = linear_ws(ws_base, S, El);
+    produce(x, cnt, S, El, self_rank, H, H_out, W, y, ws, blockIdx.x, gridDim.x, false, false, 1,
+            nullptr, nullptr, lds);
+}
+
+__global__ __launch_bounds__(kThreads) void expert_return_kernel(
+    const uint16_t *__restrict__ x, const int32_t *__restrict__ cnt, int32_t S, int32_t El,
+    int32_t self_rank, int32_t H, int32_t H_out, const uint16_t *__restrict__ W,
+    uint16_t *__restrict__ y, uint16_t *__restrict__ ret, int32_t band_group,
+    int32_t consumers, int32_t *__restrict__ ws_base)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+    __shared__ int32_t task_ok;
+    const LinearWs ws = linear_ws(ws_base, S, El);
+    const int32_t producers = (int32_t)gridDim.x - consumers;
+    if ((int32_t)blockIdx.x < producers) {
+        produce(x, cnt, S, El, self_rank, H, H_out, W, y, ws, blockIdx.x, producers, true,
+                consumers == 0, band_group, ret, &task_ok, lds);
+        return;
+    }
+    // consumer: tasks c, c + consumers, ... in remote-first order
+    const int32_t nct = H_out / kBN;
+    const int32_t n_tasks = ws.counts[1];
+    for (int32_t task = (int32_t)blockIdx.x - producers; task < n_tasks; task += consumers) {
+        int32_t b0, b1;
+        task_bands(ws, S, El, band_group, task, &b0, &b1);
+        if (threadIdx.x == 0) {
+            // poll with relaxed loads (they read the coherent copy without
+            // invalidating any cache the producers rely on); acquire once, below
+            int32_t ok = 1;
+            for (int32_t band = b0; band < b1 && ok; ++band) {
+                int spins = 0;
+                while (__hip_atomic_load(ws.flags + band, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nct) {
+                    if (++spins > kSpinLimit) {
+                        ok = 0;
+                        __hip_atomic_store(ws.status, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        break;
+                    }
+                    __builtin_amdgcn_s_sleep(8);
+                }
+            }
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+            task_ok = ok;
+        }
+        __syncthreads();
+        if (task_ok)
+            return_rows(ws, cnt, S, El, self_rank, H_out, b0, b1, y, ret);
+        __syncthreads();  // task_ok is rewritten for the next task
+    }
+}
+
+// resident blocks per device (occupancy x CUs) for each kernel, 0 = not yet asked
+int g_linear_slots[64], g_return_slots[64];
+
+hipError_t resident_blocks(const void *kernel, int *cache, int *slots)
+{
+    int dev;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return err;
+    if (dev < 64 && cache[dev] > 0) {
+        *slots = cache[dev];
+        return hipSuccess;
+    }
+    int per_cu = 0, cus = 0;
+    if ((err = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0)) != hipSuccess)
+        return err;
+    if ((err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess)
+        return err;
+    *slots = per_cu * cus;
+    if (dev < 64)
+        cache[dev] = *slots;
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t expert_return_slots(int *slots)
+{
+    return resident_blocks(reinterpret_cast<const void *>(expert_return_kernel), g_return_slots, slots);
+}
+
+size_t expert_linear_workspace_bytes(int32_t S, int32_t El, int64_t max_rows)
+{
+    return (size_t)linear_ws_words(S, El, max_rows) * sizeof(int32_t);
+}
+
+hipError_t launch_expert_linear(const uint16_t *recv, const int32_t *cnt, int32_t S, int32_t El,
+                                int32_t H, int32_t H_out, const uint16_t *W, int64_t max_rows,
+                                uint16_t *y, int32_t *workspace, hipStream_t stream)
+{
+    hipLaunchKernelGGL(linear_table_kernel, dim3(1), dim3(kTableThreads), 0, stream, cnt, S, El,
+                       S - 1, 1, max_rows, max_bands(S, El, max_rows), workspace);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || max_rows == 0)
+        return err;
+    int slots = 0;
+    if ((err = resident_blocks(reinterpret_cast<const void *>(expert_linear_kernel), g_linear_slots,
+                               &slots)) != hipSuccess)
+        return err;
+    const int64_t tiles = max_bands(S, El, max_rows) * (H_out / kBN);
+    const int grid = (int)(tiles < slots ? tiles : slots);
+    hipLaunchKernelGGL(expert_linear_kernel, dim3(grid), dim3(kThreads), 0, stream, recv, cnt, S,
+                       El, S - 1, H, H_out, W, y, workspace);
+    return hipGetLastError();
+}
+
+hipError_t launch_expert_return(const uint16_t *recv, const int32_t *cnt, int32_t S, int32_t El,
+                                int32_t H, int32_t H_out, const uint16_t *W, int64_t max_rows,
+                                int32_t self_rank, int32_t consumers, int32_t band_group,
+                                uint16_t *y, uint16_t *ret, int32_t *workspace,
+                                hipStream_t stream, int32_t *grid_used)
+{
+    hipLaunchKernelGGL(linear_table_kernel, dim3(1), dim3(kTableThreads), 0, stream, cnt, S, El,
+                       self_rank, band_group, max_rows, max_bands(S, El, max_rows), workspace);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || max_rows == 0)
+        return err;
+    int slots = 0;
+    if ((err = resident_blocks(reinterpret_cast<const void *>(expert_return_kernel), g_return_slots,
+                               &slots)) != hipSuccess)
+        return err;
+    if (consumers < 0 || consumers >= slots)
+        return hipErrorInvalidValue;
+    *grid_used = slots;
+    void *args[] = {(void *)&recv, (void *)&cnt, (void *)&S, (void *)&El, (void *)&self_rank,
+                    (void *)&H, (void *)&H_out, (void *)&W, (void *)&y, (void *)&ret,
+                    (void *)&band_group, (void *)&consumers, (void *)&workspace};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(expert_return_kernel),
+                                      dim3(slots), dim3(kThreads), args, 0, stream);
+}
+
+}  // namespace moe

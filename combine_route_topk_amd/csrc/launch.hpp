@@ -61,6 +61,18 @@ hipError_t launch_dispatch_permute_fp8(const uint16_t *x, const int32_t *pos, in
 hipError_t launch_fp8_dequant(const uint8_t *rows, const int32_t *n_rows, int64_t max_rows,
                               int32_t H, uint16_t *out, hipStream_t stream);
 
+// Tile-signalled return with a stand-in expert GEMM (expert.hip).
+size_t expert_linear_workspace_bytes(int32_t S, int32_t El, int64_t max_rows);
+hipError_t expert_return_slots(int *slots);
+hipError_t launch_expert_linear(const uint16_t *recv, const int32_t *cnt, int32_t S, int32_t El,
+                                int32_t H, int32_t H_out, const uint16_t *W, int64_t max_rows,
+                                uint16_t *y, int32_t *workspace, hipStream_t stream);
+hipError_t launch_expert_return(const uint16_t *recv, const int32_t *cnt, int32_t S, int32_t El,
+                                int32_t H, int32_t H_out, const uint16_t *W, int64_t max_rows,
+                                int32_t self_rank, int32_t consumers, int32_t band_group,
+                                uint16_t *y, uint16_t *ret, int32_t *workspace,
+                                hipStream_t stream, int32_t *grid_used);
+
 // Receive-side regroup (regroup.hip).
 size_t regroup_workspace_bytes(int32_t S, int32_t El);
 hipError_t launch_recv_regroup_layout(const int32_t *recv_counts, int32_t S, int32_t El,

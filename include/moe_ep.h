@@ -364,6 +364,88 @@ moe_status_t moe_recv_ungroup(const uint16_t *grouped, const int32_t *recv_pos,
                               const int32_t *n_rows, int64_t max_rows, int32_t H,
                               uint16_t *out, void *stream);
 
+/*
+ * Tile-signalled return: a stand-in expert computation on a destination's
+ * receive buffer whose output tiles are returned to their sources as soon
+ * as they are ready.
+ *
+ * Defined by: thecoregrid "Mixture-of-experts acceleration through
+ * overlap" (a producer GEMM and a consumer synchronised per tile: the GEMM
+ * epilogue publishes a readiness flag per tile, and the consumer starts a
+ * transfer once enough row bands are ready, several bands per transfer;
+ * each tile belongs to one destination, the remote-owner-aligned layout,
+ * and remote tiles are computed first; compute units are split between the
+ * roles); aicassindra "gpu_moe_all_to_all", "Overlapping dispatch with
+ * expert compute" (dispatch, compute and combine form a strict chain).
+ *
+ * The receive buffer recv [max_rows][H] bf16 is laid out as in
+ * moe_recv_regroup_layout: S source segments in order, each holding
+ * recv_counts[s][l] rows of local expert l, l ascending. The stand-in
+ * expert is one linear map per local expert, W [E_l][H_out][H] bf16
+ * (output-major, as a linear layer's weight):
+ *   y[i][o] = bf16( sum_h recv[i][h] * W[l][o][h] )
+ * accumulated in fp32 (MFMA) and rounded once, to nearest even, for every
+ * row i < N = sum of the counts (rows past N are not written). Tiles are
+ * 128 rows of one (source, expert) block by 128 output columns, so every
+ * tile goes back to exactly one source.
+ *
+ * Limits: as moe_recv_regroup_layout for S and E_l; H % 64 == 0,
+ * H_out % 128 == 0, both <= 65536; max_rows < 2^31. Buffers 16-byte
+ * aligned; recv, W, y and ret do not overlap. Device-side precondition:
+ * N <= max_rows. If it fails, nothing is computed and the status word
+ * (below) reads 2.
+ *
+ * Workspace: moe_expert_linear_workspace_size() bytes, 16-byte aligned.
+ * Its first int32 is a status word, which the caller may read after the
+ * call completes: 0 = done; 1 = a consumer wait exceeded its bound and
+ * some rows of ret were not returned; 2 = counts total more than max_rows.
+ */
+moe_status_t moe_expert_linear_workspace_size(int32_t S, int32_t E_l, int64_t max_rows,
+                                              size_t *bytes);
+
+/* moe_expert_linear -- y only, as one grouped GEMM launch (the schedule
+ * without overlap: the return starts after it completes). */
+moe_status_t moe_expert_linear(const uint16_t *recv, const int32_t *recv_counts, int32_t S,
+                               int32_t E_l, int32_t H, int32_t H_out, const uint16_t *W,
+                               int64_t max_rows, uint16_t *y, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/*
+ * moe_expert_linear_return -- y as above, and ret [max_rows][H_out] bf16
+ * with ret[i] = y[i] for i < N: the rows returned to their sources (on one
+ * device the sources' return buffers are partitions of ret, in the same
+ * row positions, so moe_combine_reduce reads ret unchanged).
+ *
+ * One cooperative launch of moe_expert_return_slots() blocks, all resident.
+ *   - Work units (a band -- the 128-row tile of one (source, expert) block --
+ *     by up to 4 column tiles) go in remote-first order: sources
+ *     self_rank+1, self_rank+2, ... (mod S), self_rank last.
+ *   - After each unit a producer release-adds its column tiles to the
+ *     band's count.
+ *   - A task is up to band_group consecutive bands of one source: one
+ *     contiguous copy of rows from y to ret.
+ * consumer_blocks > 0: that many blocks only return rows. Each takes tasks
+ *   in order, waits until every band of the task has all its column tiles,
+ *   and copies it. Every wait is bounded; on expiry the status word reads 1
+ *   and that task is skipped, so no call hangs.
+ * consumer_blocks == 0: every block computes. The unit that completes a
+ *   band counts it toward its task, and the block that completes a task's
+ *   last band copies the task itself. Nothing waits.
+ * Errors: as moe_expert_linear; MOE_ERR_INVALID_ARG for self_rank outside
+ *   [0, S), consumer_blocks < 0 or band_group < 1; MOE_ERR_UNSUPPORTED when
+ *   consumer_blocks >= moe_expert_return_slots().
+ */
+moe_status_t moe_expert_linear_return(const uint16_t *recv, const int32_t *recv_counts,
+                                      int32_t S, int32_t E_l, int32_t H, int32_t H_out,
+                                      const uint16_t *W, int64_t max_rows, int32_t self_rank,
+                                      int32_t consumer_blocks, int32_t band_group, uint16_t *y,
+                                      uint16_t *ret, void *workspace, size_t workspace_bytes,
+                                      void *stream);
+
+/* Blocks of one moe_expert_linear_return launch on the current device
+ * (resident blocks per compute unit x compute units). */
+moe_status_t moe_expert_return_slots(int32_t *slots);
+
 /* moe_status_string -- a static, human-readable name for a status. */
 const char *moe_status_string(moe_status_t status);
 

@@ -221,6 +221,51 @@ def test_fp8_validation(moe):
     assert deq(n=MIS) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_expert_linear_validation(moe):
+    lib = moe.lib
+    SE = 64 * 8
+    # status, counts, band bound; block rows and band prefix; task prefix; band and task counts
+    assert moe.moe_expert_linear_workspace_size(64, 8, 327680) == 4 * (4 + 2 * SE + 1 + 64 + 1 + 2 * (SE + 2560))
+    assert moe.moe_expert_linear_workspace_size(4, 4, 0) == 4 * (4 + 32 + 1 + 5 + 2 * 16)
+    n = ctypes.c_size_t(0)
+    assert lib.moe_expert_linear_workspace_size(0, 4, 10, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_expert_linear_workspace_size(128, 64, 10, ctypes.byref(n)) == moe.MOE_ERR_UNSUPPORTED
+    assert lib.moe_expert_linear_workspace_size(4, 4, -1, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    ws = moe.moe_expert_linear_workspace_size(4, 4, 512)
+
+    def lin(recv=FAKE, cnt=FAKE, S=4, El=4, H=256, H_out=256, W=FAKE, rows=512, y=FAKE, w=FAKE, wb=ws):
+        return lib.moe_expert_linear(recv, cnt, S, El, H, H_out, W, rows, y, w, wb, None)
+
+    assert lin(S=0) == moe.MOE_ERR_INVALID_ARG
+    assert lin(rows=-1) == moe.MOE_ERR_INVALID_ARG
+    assert lin(rows=2 ** 31) == moe.MOE_ERR_UNSUPPORTED
+    assert lin(H=96) == moe.MOE_ERR_UNSUPPORTED            # H % 64
+    assert lin(H_out=192) == moe.MOE_ERR_UNSUPPORTED       # H_out % 128
+    assert lin(H_out=0) == moe.MOE_ERR_UNSUPPORTED
+    assert lin(cnt=None) == moe.MOE_ERR_INVALID_ARG
+    assert lin(recv=None) == moe.MOE_ERR_INVALID_ARG
+    assert lin(W=None) == moe.MOE_ERR_INVALID_ARG
+    assert lin(y=None) == moe.MOE_ERR_INVALID_ARG
+    assert lin(recv=FAKE + 8) == moe.MOE_ERR_INVALID_ARG
+    assert lin(W=FAKE + 8) == moe.MOE_ERR_INVALID_ARG
+    assert lin(cnt=MIS) == moe.MOE_ERR_INVALID_ARG
+    assert lin(w=None) == moe.MOE_ERR_WORKSPACE
+    assert lin(wb=ws - 4) == moe.MOE_ERR_WORKSPACE
+
+    def ret(self_rank=0, consumers=8, group=4, r=FAKE, recv=FAKE, H=256):
+        return lib.moe_expert_linear_return(recv, FAKE, 4, 4, H, 256, FAKE, 512, self_rank, consumers,
+                                            group, FAKE, r, FAKE, ws, None)
+
+    assert ret(H=96) == moe.MOE_ERR_UNSUPPORTED
+    assert ret(recv=None) == moe.MOE_ERR_INVALID_ARG
+    assert ret(self_rank=-1) == moe.MOE_ERR_INVALID_ARG
+    assert ret(self_rank=4) == moe.MOE_ERR_INVALID_ARG
+    assert ret(consumers=-1) == moe.MOE_ERR_INVALID_ARG
+    assert ret(group=0) == moe.MOE_ERR_INVALID_ARG
+    assert ret(r=None) == moe.MOE_ERR_INVALID_ARG
+    assert ret(r=FAKE + 8) == moe.MOE_ERR_INVALID_ARG
+
+
 def test_binding_refuses_host_tensors(moe):
     import torch
     with pytest.raises(ValueError):
