@@ -5,7 +5,10 @@ moe_route_topk -> moe_dispatch_layout -> moe_dispatch_permute ->
 moe_combine_reduce (the expert is the identity: combine reads the send
 buffer). W untimed warm-up steps, then exactly K timed steps between
 device synchronisations with HIP events only at the two ends (an event
-between calls leaves the GPU idle for a few microseconds). A second pass of
+between calls leaves the GPU idle for a few microseconds). The steps are
+eager launches; --graph times replays of a HIP graph that holds the four
+launches instead (on MI355X a replay cost 40 us where the four eager
+launches of the decode workload cost 18 us, so eager is the default). A second pass of
 K steps records an event pair around every call, on the stream the kernels
 run on, for the per-call durations and the roofline of the dominant kernel.
 
@@ -72,6 +75,9 @@ def parse():
     p.add_argument("--workload", default="fine_grained",
                    help="one of " + ", ".join(w.name for w in synthetic.WORKLOADS.values()))
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--graph", action="store_true",
+                   help="time replays of a captured HIP graph of the step instead of eager launches "
+                        "(on MI355X with ROCm 7 a replay costs more than four eager launches)")
     p.add_argument("--no-fp8", action="store_true",
                    help="skip the FP8-payload step measurement (reported under next_rows)")
     p.add_argument("--no-tile-return", action="store_true",
@@ -393,21 +399,24 @@ def main():
         if rc != moe.MOE_OK:
             raise RuntimeError(f"{name}: {moe.moe_status_string(rc)}")
 
-    calls = [
-        ("route", lambda: check("route", lib.moe_route_topk(
-            P(logits), P(bias), T, E, k, moe.MOE_ROUTE_NORMALIZE, P(idx), P(wt), sp))
-         if groups is None else check("route", lib.moe_route_topk_grouped(
-            P(logits), P(bias), T, E, k, groups[0], groups[1], moe.MOE_ROUTE_NORMALIZE, P(idx),
-            P(wt), sp))),
-        ("layout", lambda: check("layout", lib.moe_dispatch_layout(
-            P(idx), T, E, k, R, C, P(lay["expert_demand"]), P(lay["expert_counts"]),
-            P(lay["expert_offsets"]), P(lay["dest_counts"]), P(lay["dest_offsets"]),
-            P(lay["pos"]), P(lay["send_src"]), P(ws), ws.numel(), sp))),
-        ("permute", lambda: check("permute", lib.moe_dispatch_permute(
-            P(x), P(lay["pos"]), T, H, k, P(send), send_rows, sp))),
-        ("combine", lambda: check("combine", lib.moe_combine_reduce(
-            P(send), send_rows, P(lay["pos"]), P(wt), P(sh), P(res), T, H, k, 0, P(out), sp))),
-    ]
+    def make_calls(sp):
+        return [
+            ("route", lambda: check("route", lib.moe_route_topk(
+                P(logits), P(bias), T, E, k, moe.MOE_ROUTE_NORMALIZE, P(idx), P(wt), sp))
+             if groups is None else check("route", lib.moe_route_topk_grouped(
+                P(logits), P(bias), T, E, k, groups[0], groups[1], moe.MOE_ROUTE_NORMALIZE, P(idx),
+                P(wt), sp))),
+            ("layout", lambda: check("layout", lib.moe_dispatch_layout(
+                P(idx), T, E, k, R, C, P(lay["expert_demand"]), P(lay["expert_counts"]),
+                P(lay["expert_offsets"]), P(lay["dest_counts"]), P(lay["dest_offsets"]),
+                P(lay["pos"]), P(lay["send_src"]), P(ws), ws.numel(), sp))),
+            ("permute", lambda: check("permute", lib.moe_dispatch_permute(
+                P(x), P(lay["pos"]), T, H, k, P(send), send_rows, sp))),
+            ("combine", lambda: check("combine", lib.moe_combine_reduce(
+                P(send), send_rows, P(lay["pos"]), P(wt), P(sh), P(res), T, H, k, 0, P(out), sp))),
+        ]
+
+    calls = make_calls(sp)
 
     def step(evs=None):
         for i, (_, fn) in enumerate(calls):
@@ -424,18 +433,42 @@ def main():
 
     # pass 1 (the measurement): K steps between synchronisations, with events
     # only at the two ends -- an event between calls costs the GPU a few us
-    # of idle time, which would be charged to the path
-    t_beg, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    t_beg.record(stream)
-    for _ in range(args.steps):
-        step()
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t_wall
-    ms_per_step = t_beg.elapsed_time(t_end) / args.steps
-    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step (wall {wall_s / args.steps * 1e6:.1f} us/step)")
+    # of idle time, which would be charged to the path. With --graph each step
+    # is one replay of a HIP graph holding the four launches (captured once,
+    # outside the timed region); the eager loop is timed and reported anyway.
+    def timed_steps(run_one):
+        t_beg, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        t_beg.record(stream)
+        for _ in range(args.steps):
+            run_one()
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        return t_beg.elapsed_time(t_end) / args.steps, (time.perf_counter() - t_wall) / args.steps
+
+    ms_eager, wall_eager = timed_steps(step)
+    log(f"eager: {args.steps} steps, {ms_eager * 1e3:.1f} us/step (wall {wall_eager * 1e6:.1f} us/step)")
+    graph = None
+    if args.graph:
+        gstream = torch.cuda.Stream()
+        gcalls = make_calls(gstream.cuda_stream)
+        torch.cuda.synchronize()
+        with torch.cuda.stream(gstream):
+            for _, fn in gcalls:
+                fn()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=gstream):
+            for _, fn in gcalls:
+                fn()
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        ms_graph, wall_graph = timed_steps(graph.replay)
+        log(f"graph: {args.steps} replays, {ms_graph * 1e3:.1f} us/step (wall {wall_graph * 1e6:.1f} us/step)")
+    ms_per_step = ms_eager if graph is None else ms_graph
+    log(f"timed {args.steps} steps: {ms_per_step * 1e3:.1f} us/step")
 
     # pass 2: K more steps with an event pair around every call, for the
     # per-call durations and the roofline of the dominant kernel
@@ -511,6 +544,8 @@ def main():
         "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "tokens_per_s": round(tokens_per_s, 1),
         "per_call_us": {n: round(v * 1e3, 2) for n, v in per_call_ms.items()},
+        "timing": "one HIP graph replay per step (four launches)" if graph is not None else "eager launches",
+        "ms_per_step_eager": round(ms_eager, 5),
         "per_call_note": "second pass of the same K steps with an event pair around every call",
         "per_call_GBps": {n: round(nbytes[n] / (per_call_ms[n] * 1e-3) / 1e9, 1) for n in nbytes},
         "roofline": roofline,

@@ -9,9 +9,10 @@
 // 512 experts (an always-active shared expert next to the routed ones).
 //
 // Block (t, y) produces a 4 KiB column slab of out[t]: each lane owns 8
-// consecutive elements. The kept rows' positions and weights are uniform
-// per block (scalar loads); all k 16-byte row loads are issued before the
-// first multiply so that k loads per lane are in flight. Accumulation is
+// consecutive elements. The kept rows' positions and weights come in with
+// one vector load each (lane j holds entry j) and are broadcast as uniform
+// values; all k 16-byte row loads are issued before the first multiply so
+// that k loads per lane are in flight. Accumulation is
 // float32, one fused multiply-add per kept replica in ascending j, then
 // + shared, then + residual, then a single rounding (gfx950's packed
 // round-to-nearest-even bf16 convert) or a float32 store.
@@ -40,8 +41,18 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
 {
     const int64_t t = blockIdx.x;
     const int32_t c = blockIdx.y * kRowThreads + threadIdx.x;
-    if (c >= C16)
-        return;
+    // the token's k positions and weights: lane j < k of each wave loads entry
+    // j (two vector loads in flight at once) and readlane makes each uniform,
+    // instead of 2k scalar loads that each wait for the one before. Every lane
+    // stays until the broadcasts are done (a lane that left early could not be
+    // read).
+    const int lane = threadIdx.x & (kWave - 1);
+    int32_t pl = -1;
+    float wl = 0.f;
+    if (lane < k) {
+        pl = pos[t * k + lane];
+        wl = topk_w[t * k + lane];
+    }
     int32_t p[KMAX];
     float wt[KMAX];
 #pragma unroll
@@ -49,13 +60,15 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
         p[j] = -1;
         wt[j] = 0.f;
         if (j < k) {
-            const int32_t q = pos[t * k + j];
+            const int32_t q = (int32_t)readlane_u32((uint32_t)pl, j);
             if (q >= 0 && q < y_rows) {
                 p[j] = q;
-                wt[j] = topk_w[t * k + j];
+                wt[j] = __uint_as_float(readlane_u32(__float_as_uint(wl), j));
             }
         }
     }
+    if (c >= C16)
+        return;
     u32x4 v[KMAX];
 #pragma unroll
     for (int j = 0; j < KMAX; ++j)

@@ -28,19 +28,20 @@ __global__ __launch_bounds__(kRowThreads) void permute_kernel(
 {
     const int64_t t = blockIdx.x;
     const int32_t c = blockIdx.y * kRowThreads + threadIdx.x;
-    const int32_t *pr = pos + t * k;
-    bool any = false;
-    for (int j = 0; j < k; ++j) {
-        const int32_t p = pr[j];
-        any |= p >= 0 && p < send_rows;
-    }
-    if (!any || c >= C16)
+    // the token's k positions in one vector load (lane j < k holds entry j),
+    // broadcast with readlane, instead of k scalar loads that wait in turn
+    const int lane = threadIdx.x & (kWave - 1);
+    const int32_t pl = lane < k ? pos[t * k + lane] : -1;
+    const bool kept = pl >= 0 && pl < send_rows;
+    if (ballot64(kept) == 0)  // every replica dropped: the same for the whole block
         return;
-    const u32x4 v = x[t * C16 + c];
-    for (int j = 0; j < k; ++j) {
-        const int32_t p = pr[j];
-        if (p >= 0 && p < send_rows)
-            store_stream(send + (int64_t)p * C16 + c, v);
+    if (c < C16) {
+        const u32x4 v = x[t * C16 + c];
+        for (int j = 0; j < k; ++j) {
+            const int32_t p = (int32_t)readlane_u32((uint32_t)pl, j);
+            if (p >= 0 && p < send_rows)
+                store_stream(send + (int64_t)p * C16 + c, v);
+        }
     }
 }
 

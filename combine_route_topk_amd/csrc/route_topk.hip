@@ -18,7 +18,9 @@
 // otherwise lane l owns experts l, l + 64, ... with 4-byte loads. On MI355X
 // the 16-byte form reads the logits at ~6.9 TB/s against ~2 TB/s for the
 // 4-byte form, which made the load phase the bottleneck of this kernel.
-// Either way a lane's slots are in ascending expert order. Scores become
+// Either way a lane's slots are in ascending expert order. For small rows
+// (E <= 128) each 32-lane half of the wave routes its own token, with the
+// same steps over half-wave reductions. Scores become
 // order-preserving 32-bit keys and each lane keeps its two best remaining
 // (key, id) candidates, built without branches. A selection round is a
 // wave-wide 32-bit maximum by DPP (six fused max steps, one readlane), a
@@ -36,7 +38,7 @@ namespace moe {
 namespace {
 
 constexpr int kRouteThreads = 256;
-constexpr int kTokensPerBlock = kRouteThreads / kWave;
+constexpr int kWavesPerBlock = kRouteThreads / kWave;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -51,31 +53,84 @@ __device__ __forceinline__ uint32_t score_key(float s)
     return s != s ? 1u : k;
 }
 
-// Expert id held in slot i of lane `lane`, and the lane that holds expert e.
-template <int VEC>
-__device__ __forceinline__ uint32_t slot_id(int i, int lane)
+// TPW tokens per wave: token h of the wave lives on lanes [h*HW, (h+1)*HW),
+// HW = 64 / TPW lanes per token.
+template <int TPW>
+struct Group {
+    static constexpr int HW = kWave / TPW;
+    // reduce within each token's lanes; every lane gets its own token's result
+    template <class Op>
+    __device__ __forceinline__ static uint32_t reduce(uint32_t v, uint32_t identity, Op op)
+    {
+        v = op(v, dpp::mov<dpp::kQuadSwap1>(v, identity));
+        v = op(v, dpp::mov<dpp::kQuadSwap2>(v, identity));
+        v = op(v, dpp::mov<dpp::kRowHalfMirror>(v, identity));
+        v = op(v, dpp::mov<dpp::kRowMirror>(v, identity));
+        v = op(v, dpp::mov<dpp::kRowBcast15, 0xA>(v, identity));
+        if (TPW == 1) {
+            v = op(v, dpp::mov<dpp::kRowBcast31, 0xC>(v, identity));
+            return readlane_u32(v, kWave - 1);
+        }
+        // lane 31 holds rows 0-1 (the first token), lane 63 rows 2-3
+        const uint32_t lo = readlane_u32(v, 31), hi = readlane_u32(v, 63);
+        return (threadIdx.x & (kWave - 1)) < 32 ? lo : hi;
+    }
+    __device__ __forceinline__ static uint32_t max_u32(uint32_t v)
+    {
+        return reduce(v, 0u, [](uint32_t a, uint32_t b) { return max(a, b); });
+    }
+    __device__ __forceinline__ static uint32_t min_u32(uint32_t v)
+    {
+        return reduce(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return min(a, b); });
+    }
+    __device__ __forceinline__ static float max_f32(float v)
+    {
+        return __uint_as_float(reduce(__float_as_uint(v), __float_as_uint(-INFINITY),
+                                      [](uint32_t a, uint32_t b) {
+                                          return __float_as_uint(fmaxf(__uint_as_float(a), __uint_as_float(b)));
+                                      }));
+    }
+    __device__ __forceinline__ static float sum_f32(float v)
+    {
+        return __uint_as_float(reduce(__float_as_uint(v), 0u, [](uint32_t a, uint32_t b) {
+            return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
+        }));
+    }
+};
+
+// Expert id held in slot i of in-token lane `gl`, and the in-token lane that
+// holds expert e (HW lanes per token).
+template <int VEC, int HW>
+__device__ __forceinline__ uint32_t slot_id(int i, int gl)
 {
-    return VEC == 4 ? (uint32_t)((i / 4) * 4 * kWave + 4 * lane + (i % 4))
-                    : (uint32_t)(i * kWave + lane);
+    return VEC == 4 ? (uint32_t)((i / 4) * 4 * HW + 4 * gl + (i % 4)) : (uint32_t)(i * HW + gl);
 }
-template <int VEC>
+template <int VEC, int HW>
 __device__ __forceinline__ int owner_lane(uint32_t e)
 {
-    return VEC == 4 ? (int)((e >> 2) & (kWave - 1)) : (int)(e & (kWave - 1));
+    return VEC == 4 ? (int)((e >> 2) & (HW - 1)) : (int)(e & (HW - 1));
 }
 
-// NSLOT keys per lane; VEC = 4 (16-byte loads) or 1 (4-byte loads)
-template <int NSLOT, int VEC, bool NORMALIZE>
+// NSLOT keys per lane; VEC = 4 (16-byte loads) or 1 (4-byte loads); TPW
+// tokens per wave (2: each 32-lane half routes its own token, halving the
+// cost of the selection rounds per token)
+template <int NSLOT, int VEC, bool NORMALIZE, int TPW>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int64_t T, int32_t E,
     int32_t k, int32_t n_groups, int32_t topk_groups, int32_t *__restrict__ topk_idx,
     float *__restrict__ topk_w)
 {
+    using G = Group<TPW>;
+    constexpr int HW = G::HW;
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t t = (int64_t)blockIdx.x * kTokensPerBlock + (threadIdx.x / kWave);
-    if (t >= T)
-        return;  // t is uniform across the wave: whole waves leave together
-    const float *row = logits + t * E;
+    const int gl = lane & (HW - 1);       // lane within its token
+    const int gbase = lane - gl;          // first lane of its token
+    const int64_t t0 = ((int64_t)blockIdx.x * kWavesPerBlock + threadIdx.x / kWave) * TPW;
+    if (t0 >= T)
+        return;  // uniform across the wave: whole waves leave together
+    const int64_t t = t0 + lane / HW;
+    const bool valid = t < T;             // the second token of the last wave may not exist
+    const float *row = logits + (valid ? t : t0) * E;
 
     uint32_t key[NSLOT];
     if (VEC == 4) {
@@ -83,9 +138,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
         const f32x4 *bias4 = reinterpret_cast<const f32x4 *>(bias);
 #pragma unroll
         for (int g = 0; g < NSLOT / 4; ++g) {
-            if (g * 4 * kWave + 4 * lane < E) {
-                const f32x4 v = __builtin_nontemporal_load(row4 + g * kWave + lane);
-                const f32x4 b = bias ? bias4[g * kWave + lane] : f32x4{0.f, 0.f, 0.f, 0.f};
+            if (valid && g * 4 * HW + 4 * gl < E) {
+                const f32x4 v = __builtin_nontemporal_load(row4 + g * HW + gl);
+                const f32x4 b = bias ? bias4[g * HW + gl] : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
                     key[4 * g + c] = score_key((bias ? v[c] + b[c] : v[c]) + 0.0f);
@@ -98,8 +153,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     } else {
 #pragma unroll
         for (int i = 0; i < NSLOT; ++i) {
-            const int e = i * kWave + lane;
-            if (e < E) {
+            const int e = i * HW + gl;
+            if (valid && e < E) {
                 const float v = row[e];
                 key[i] = score_key((bias ? v + bias[e] : v) + 0.0f);
             } else {
@@ -110,30 +165,33 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
 
     if (n_groups > 0) {
         // group-limited routing: rank the n_groups contiguous expert groups
-        // by their best key (lane g holds group g's), keep the best
+        // by their best key (in-token lane g holds group g's), keep the best
         // topk_groups -- ties to the lower group, i.e. the lower lane -- and
         // drop every expert outside them
         const int32_t gsize = E / n_groups;
         int gid[NSLOT];
 #pragma unroll
         for (int i = 0; i < NSLOT; ++i)
-            gid[i] = (int)(slot_id<VEC>(i, lane) / (uint32_t)gsize);
+            gid[i] = (int)(slot_id<VEC, HW>(i, gl) / (uint32_t)gsize);
         uint32_t my_gkey = 0u;
         for (int g = 0; g < n_groups; ++g) {
             uint32_t v = 0u;
 #pragma unroll
             for (int i = 0; i < NSLOT; ++i)
                 v = gid[i] == g ? max(v, key[i]) : v;
-            const uint32_t best = wave_max_u32(v);
-            my_gkey = lane == g ? best : my_gkey;
+            const uint32_t best = G::max_u32(v);
+            my_gkey = gl == g ? best : my_gkey;
         }
         uint64_t chosen = 0;
         for (int m = 0; m < topk_groups; ++m) {
-            const uint32_t best = wave_max_u32(my_gkey);
-            const uint64_t holders = ballot64(my_gkey == best && lane < n_groups);
-            const int g = __ffsll((unsigned long long)holders) - 1;
+            const uint32_t best = G::max_u32(my_gkey);
+            const uint64_t holders = ballot64(my_gkey == best && gl < n_groups);
+            // the lowest holding lane of each token's lanes
+            const uint64_t mine = TPW == 1 ? holders
+                                           : (gbase == 0 ? holders & 0xFFFFFFFFull : holders >> 32);
+            const int g = __ffsll((unsigned long long)mine) - 1;
             chosen |= 1ull << g;
-            my_gkey = lane == g ? 0u : my_gkey;
+            my_gkey = gl == g ? 0u : my_gkey;
         }
 #pragma unroll
         for (int i = 0; i < NSLOT; ++i)
@@ -142,10 +200,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
 
     // the lane's two best entries; ascending i is ascending id, so strict
     // comparisons keep the smaller id first among equal keys
-    uint32_t c1k = key[0], c1i = slot_id<VEC>(0, lane), c2k = 0u, c2i = 0xFFFFFFFFu;
+    uint32_t c1k = key[0], c1i = slot_id<VEC, HW>(0, gl), c2k = 0u, c2i = 0xFFFFFFFFu;
 #pragma unroll
     for (int i = 1; i < NSLOT; ++i) {
-        const uint32_t kk = key[i], id = slot_id<VEC>(i, lane);
+        const uint32_t kk = key[i], id = slot_id<VEC, HW>(i, gl);
         const bool gt1 = kk > c1k, gt2 = kk > c2k;
         c2k = gt1 ? c1k : (gt2 ? kk : c2k);
         c2i = gt1 ? c1i : (gt2 ? id : c2i);
@@ -155,18 +213,31 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
 
     uint32_t my_e = 0;
     for (int j = 0; j < k; ++j) {
-        const uint32_t best = wave_max_u32(c1k);
+        const uint32_t best = G::max_u32(c1k);
         const uint64_t holders = ballot64(c1k == best);
         int owner;
         uint32_t ew;
-        if (__popcll(holders) == 1) {
-            owner = __ffsll((unsigned long long)holders) - 1;
-            ew = readlane_u32(c1i, owner);
-        } else {  // several lanes hold an equal key: the smallest id wins
-            ew = wave_min_u32(c1k == best ? c1i : 0xFFFFFFFFu);
-            owner = owner_lane<VEC>(ew);
+        bool unique;
+        if (TPW == 1)
+            unique = __popcll(holders) == 1;
+        else
+            unique = __popcll(holders & 0xFFFFFFFFull) == 1 && __popcll(holders >> 32) == 1;
+        if (unique) {
+            if (TPW == 1) {
+                owner = __ffsll((unsigned long long)holders) - 1;
+                ew = readlane_u32(c1i, owner);
+            } else {
+                const int o0 = __ffsll((unsigned long long)(holders & 0xFFFFFFFFull)) - 1;
+                const int o1 = 32 + __ffsll((unsigned long long)(holders >> 32)) - 1;
+                const uint32_t e0 = readlane_u32(c1i, o0), e1 = readlane_u32(c1i, o1);
+                owner = gbase == 0 ? o0 : o1;
+                ew = gbase == 0 ? e0 : e1;
+            }
+        } else {  // several lanes of a token hold an equal key: the smallest id wins
+            ew = G::min_u32(c1k == best ? c1i : 0xFFFFFFFFu);
+            owner = gbase + owner_lane<VEC, HW>(ew);
         }
-        my_e = lane == j ? ew : my_e;
+        my_e = gl == j ? ew : my_e;
         const bool own = lane == owner;
         const uint32_t gone_k = c1k, gone_i = c1i;
         c1k = own ? c2k : c1k;
@@ -178,7 +249,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
             c2i = 0xFFFFFFFFu;
 #pragma unroll
             for (int i = 0; i < NSLOT; ++i) {
-                const uint32_t id = slot_id<VEC>(i, lane);
+                const uint32_t id = slot_id<VEC, HW>(i, gl);
                 const uint32_t kk =
                     (key[i] < gone_k || (key[i] == gone_k && id > gone_i)) ? key[i] : 0u;
                 const bool gt1 = kk > c1k, gt2 = kk > c2k;
@@ -191,40 +262,43 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     }
 
     // unbiased logits of the selected experts, straight from the row
-    const bool mine = lane < k;
+    const bool mine = valid && gl < k;
     const float my_l = mine ? row[my_e] : -INFINITY;
     float w;
     if (NORMALIZE) {
-        const float m = wave_max_f32_dpp(my_l);
+        const float m = G::max_f32(my_l);
         const float u = mine ? expf(my_l - m) : 0.f;
-        w = u / wave_sum_f32_dpp(u);
+        w = u / G::sum_f32(u);
     } else {
         float lm = -INFINITY;
-        for (int e = lane; e < E; e += kWave)
-            lm = fmaxf(lm, row[e]);
-        const float M = wave_max_f32_dpp(lm);
+        if (valid)
+            for (int e = gl; e < E; e += HW)
+                lm = fmaxf(lm, row[e]);
+        const float M = G::max_f32(lm);
         float part = 0.f;
-        for (int e = lane; e < E; e += kWave)
-            part += expf(row[e] - M);
-        w = (mine ? expf(my_l - M) : 0.f) / wave_sum_f32_dpp(part);
+        if (valid)
+            for (int e = gl; e < E; e += HW)
+                part += expf(row[e] - M);
+        w = (mine ? expf(my_l - M) : 0.f) / G::sum_f32(part);
     }
     if (mine) {
-        topk_idx[t * k + lane] = (int32_t)my_e;
-        topk_w[t * k + lane] = w;
+        topk_idx[t * k + gl] = (int32_t)my_e;
+        topk_w[t * k + gl] = w;
     }
 }
 
-template <int NSLOT, int VEC>
+template <int NSLOT, int VEC, int TPW>
 hipError_t launch_slots(const float *logits, const float *bias, int64_t T, int32_t E, int32_t k,
                         int32_t n_groups, int32_t topk_groups, bool normalize, int32_t *topk_idx,
                         float *topk_w, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((T + kTokensPerBlock - 1) / kTokensPerBlock));
+    const int64_t per_block = (int64_t)kWavesPerBlock * TPW;
+    const dim3 grid((unsigned)((T + per_block - 1) / per_block));
     if (normalize)
-        hipLaunchKernelGGL((route_topk_kernel<NSLOT, VEC, true>), grid, dim3(kRouteThreads), 0,
+        hipLaunchKernelGGL((route_topk_kernel<NSLOT, VEC, true, TPW>), grid, dim3(kRouteThreads), 0,
                            stream, logits, bias, T, E, k, n_groups, topk_groups, topk_idx, topk_w);
     else
-        hipLaunchKernelGGL((route_topk_kernel<NSLOT, VEC, false>), grid, dim3(kRouteThreads), 0,
+        hipLaunchKernelGGL((route_topk_kernel<NSLOT, VEC, false, TPW>), grid, dim3(kRouteThreads), 0,
                            stream, logits, bias, T, E, k, n_groups, topk_groups, topk_idx, topk_w);
     return hipGetLastError();
 }
@@ -236,44 +310,42 @@ hipError_t launch_route_topk(const float *logits, const float *bias, int64_t T, 
                              int32_t *topk_idx, float *topk_w, hipStream_t stream)
 {
     const bool vec4 = E % 4 == 0 && (uintptr_t)logits % 16 == 0 && (uintptr_t)bias % 16 == 0;
+    // Two tokens per wave halve the selection rounds per token but double
+    // each lane's slots once the row needs more than one pass of the half
+    // wave. On MI355X two tokens per wave won at E = 64 (8.3 against 10.4 us,
+    // 16384 tokens) and lost at E = 256 and 512 (46 against 36 us, 32768
+    // tokens), so they are used only while the slots per lane stay the same:
+    // E <= 128 with 16-byte loads, E <= 32 otherwise; and lane g of a half
+    // must hold group g (<= 32 groups).
+    const bool two = (vec4 ? E <= 4 * 32 : E <= 32) && n_groups <= 32;
+#define MOE_ROUTE_ARGS logits, bias, T, E, k, n_groups, topk_groups, normalize, topk_idx, topk_w, stream
+    if (vec4 && two) {
+        return launch_slots<4, 4, 2>(MOE_ROUTE_ARGS);
+    }
     if (vec4) {
         switch ((E + 4 * kWave - 1) / (4 * kWave)) {
-        case 1:
-            return launch_slots<4, 4>(logits, bias, T, E, k, n_groups, topk_groups, normalize, topk_idx, topk_w, stream);
-        case 2:
-            return launch_slots<8, 4>(logits, bias, T, E, k, n_groups, topk_groups, normalize, topk_idx, topk_w, stream);
-        case 3:
-            return launch_slots<12, 4>(logits, bias, T, E, k, n_groups, topk_groups, normalize, topk_idx, topk_w, stream);
-        case 4:
-            return launch_slots<16, 4>(logits, bias, T, E, k, n_groups, topk_groups, normalize, topk_idx, topk_w, stream);
-        default:
-            return hipErrorInvalidValue;
+        case 1: return launch_slots<4, 4, 1>(MOE_ROUTE_ARGS);
+        case 2: return launch_slots<8, 4, 1>(MOE_ROUTE_ARGS);
+        case 3: return launch_slots<12, 4, 1>(MOE_ROUTE_ARGS);
+        case 4: return launch_slots<16, 4, 1>(MOE_ROUTE_ARGS);
+        default: return hipErrorInvalidValue;
         }
     }
+    if (two)
+        return launch_slots<1, 1, 2>(MOE_ROUTE_ARGS);
     switch ((E + kWave - 1) / kWave) {
 #define MOE_ROUTE_CASE(n) \
     case n:               \
-        return launch_slots<n, 1>(logits, bias, T, E, k, n_groups, topk_groups, normalize, topk_idx, topk_w, stream);
-        MOE_ROUTE_CASE(1)
-        MOE_ROUTE_CASE(2)
-        MOE_ROUTE_CASE(3)
-        MOE_ROUTE_CASE(4)
-        MOE_ROUTE_CASE(5)
-        MOE_ROUTE_CASE(6)
-        MOE_ROUTE_CASE(7)
-        MOE_ROUTE_CASE(8)
-        MOE_ROUTE_CASE(9)
-        MOE_ROUTE_CASE(10)
-        MOE_ROUTE_CASE(11)
-        MOE_ROUTE_CASE(12)
-        MOE_ROUTE_CASE(13)
-        MOE_ROUTE_CASE(14)
-        MOE_ROUTE_CASE(15)
-        MOE_ROUTE_CASE(16)
+        return launch_slots<n, 1, 1>(MOE_ROUTE_ARGS);
+        MOE_ROUTE_CASE(1) MOE_ROUTE_CASE(2) MOE_ROUTE_CASE(3) MOE_ROUTE_CASE(4)
+        MOE_ROUTE_CASE(5) MOE_ROUTE_CASE(6) MOE_ROUTE_CASE(7) MOE_ROUTE_CASE(8)
+        MOE_ROUTE_CASE(9) MOE_ROUTE_CASE(10) MOE_ROUTE_CASE(11) MOE_ROUTE_CASE(12)
+        MOE_ROUTE_CASE(13) MOE_ROUTE_CASE(14) MOE_ROUTE_CASE(15) MOE_ROUTE_CASE(16)
 #undef MOE_ROUTE_CASE
     default:
         return hipErrorInvalidValue;
     }
+#undef MOE_ROUTE_ARGS
 }
 
 }  // namespace moe

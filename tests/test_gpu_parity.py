@@ -242,6 +242,7 @@ SHAPES = [
     (1000, 136, 32, 32, 8, -1),   # k = E: a full sort
     (4099, 256, 1024, 32, 16, -1),  # largest E and k
     (5000, 520, 16, 2, 16, 300),  # E / R = 1, capacity
+    (333, 64, 30, 5, 3, -1),      # E = 30: two tokens per wave on 4-byte loads, odd T
     (3000, 128, 40, 3, 1, 100),   # R = 1
     (70001, 16, 32, 8, 8, -1),    # 274 tiles: several tiles per scan wave
     (2048, 64, 8, 2, 2, 0),       # capacity 0 drops everything
@@ -411,6 +412,8 @@ GROUPED = [
     (333, 70, 6, 7, 2, "uniform"),     # 4-byte route path
     (200, 64, 4, 64, 4, None),         # one expert per group: plain top-k
     (300, 64, 6, 8, 8, None),          # every group allowed: plain top-k
+    (777, 32, 5, 16, 3, "uniform"),    # two tokens per wave, 16-byte loads, odd T
+    (401, 30, 4, 5, 2, None),          # two tokens per wave, 4-byte loads, odd T
 ]
 
 
