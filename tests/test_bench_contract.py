@@ -1,0 +1,85 @@
+"""Host-side parts of bench.py that need no GPU: the one-GPU refusal, the
+algorithmic byte counts behind `value` and the roofline, workload lookup,
+and the rule that a stored counter record counts only for the kernel source
+it was taken on."""
+
+import importlib.util
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import synthetic
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def bench():
+    spec = importlib.util.spec_from_file_location("bench_under_test", os.path.join(ROOT, "bench.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_refuses_more_than_one_gpu():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_workload_lookup(bench):
+    for i, w in synthetic.WORKLOADS.items():
+        assert bench.workload_by_name(w.name) is w
+        assert bench.workload_by_name(str(i)) is w
+    with pytest.raises(SystemExit):
+        bench.workload_by_name("no_such_workload")
+
+
+def test_algorithmic_bytes_fine_grained(bench):
+    """Every array read once and written once, kept rows only (the sizes in
+    the benchmark's docstring), at the largest workload: N = T*k kept rows,
+    every token read, a shared expert and a residual."""
+    w = synthetic.WORKLOADS[5]
+    T, H, E, k, R = w.T, w.H, w.E, w.k, w.R
+    N = T * k
+    nb = bench.algorithmic_bytes(w, N, T, has_bias=False)
+    assert nb["route"] == 32768 * 512 * 4 + 2 * 32768 * 10 * 4 == 69_730_304
+    assert nb["layout"] == 2 * T * k * 4 + N * 4 + (3 * E + 2 * R + 2) * 4
+    assert nb["permute"] == T * k * 4 + T * H * 2 + N * H * 2 == 1_477_705_728
+    # send rows + shared + residual + out, and pos + weights
+    assert nb["combine"] == 2 * T * k * 4 + N * H * 2 + 3 * T * H * 2 == 1_747_451_904
+    assert sum(nb.values()) == 3_298_826_760
+
+
+def test_algorithmic_bytes_capacity_and_bias(bench):
+    w = synthetic.WORKLOADS[3]            # capacity-limited, residual, no shared expert
+    nb = bench.algorithmic_bytes(w, 8887, 7169, has_bias=True)
+    assert nb["route"] == w.T * w.E * 4 + w.E * 4 + 2 * w.T * w.k * 4
+    assert nb["permute"] == w.T * w.k * 4 + 7169 * w.H * 2 + 8887 * w.H * 2
+    assert nb["combine"] == 2 * w.T * w.k * 4 + 8887 * w.H * 2 + 2 * w.T * w.H * 2
+
+
+def test_stored_traffic_needs_matching_source(bench, tmp_path, monkeypatch):
+    kernel = "combine_kernel"
+    src = bench.KERNEL_SOURCES[kernel]
+    rec = {"source_sha256_16": bench.source_hash(src), "hbm_bytes_per_launch": 123}
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    path = tmp_path / f"traffic_{kernel}_some_workload.json"
+    path.write_text(json.dumps(rec))
+    assert bench.stored_traffic(kernel, "some_workload") == 123
+    rec["source_sha256_16"] = "0" * 16
+    path.write_text(json.dumps(rec))
+    assert bench.stored_traffic(kernel, "some_workload") is None
+    assert bench.stored_traffic(kernel, "absent_workload") is None
+
+
+def test_committed_traffic_records_match_sources(bench):
+    """The records under profiles/ were taken on the kernel sources as they
+    stand; a stale one would make the benchmark report no traffic."""
+    for kernel in bench.KERNEL_SOURCES:
+        assert bench.stored_traffic(kernel, "fine_grained") is not None, kernel
