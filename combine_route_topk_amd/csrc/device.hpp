@@ -23,43 +23,6 @@ __device__ __forceinline__ uint32_t count_below(uint64_t mask)
                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-__device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int m)
-{
-    return (uint32_t)__shfl_xor((int)v, m, kWave);
-}
-
-// Wave-wide maximum of an unsigned 64-bit value; every lane gets it.
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v)
-{
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1) {
-        uint32_t lo = shfl_xor_u32((uint32_t)v, m);
-        uint32_t hi = shfl_xor_u32((uint32_t)(v >> 32), m);
-        uint64_t o = ((uint64_t)hi << 32) | lo;
-        v = o > v ? o : v;
-    }
-    return v;
-}
-
-// Wave-wide float sum by an xor butterfly. Lanes i and i^m add the same two
-// partial sums at every step, so every lane ends with the same bits and the
-// association order is fixed (the result is reproducible).
-__device__ __forceinline__ float wave_sum_f32(float v)
-{
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        v += __shfl_xor(v, m, kWave);
-    return v;
-}
-
-__device__ __forceinline__ float wave_max_f32(float v)
-{
-#pragma unroll
-    for (int m = 32; m >= 1; m >>= 1)
-        v = fmaxf(v, __shfl_xor(v, m, kWave));
-    return v;
-}
-
 // Wave-wide inclusive prefix sum of an int (Hillis-Steele over the lanes).
 __device__ __forceinline__ int32_t wave_inclusive_sum(int32_t v)
 {
@@ -73,13 +36,13 @@ __device__ __forceinline__ int32_t wave_inclusive_sum(int32_t v)
     return v;
 }
 
-// Wave-wide reductions with DPP lane permutations, for commutative and
-// associative operations with an identity. Four steps combine pairs,
-// quads, 8-lane halves and 16-lane rows (after each step the lanes of a
-// group agree); row_bcast:15 then folds row 0 into row 1 and row 2 into row
-// 3, and row_bcast:31 folds rows 0-1 into rows 2-3, so lane 63 ends with
-// the result of the whole wave. The association order is fixed, so float
-// results are reproducible. The result is read back as a uniform value.
+// DPP lane permutations for wave reductions of commutative, associative
+// operations with an identity. Four steps combine pairs, quads, 8-lane
+// halves and 16-lane rows (after each step the lanes of a group agree);
+// row_bcast:15 then folds row 0 into row 1 and row 2 into row 3, and
+// row_bcast:31 folds rows 0-1 into rows 2-3, so lane 63 ends with the whole
+// wave's result (lanes 31 and 63 with each 32-lane half's). The association
+// order is fixed, so float results are reproducible.
 namespace dpp {
 constexpr int kQuadSwap1 = 0xB1;       // quad_perm [1,0,3,2]: lane ^ 1
 constexpr int kQuadSwap2 = 0x4E;       // quad_perm [2,3,0,1]: lane ^ 2
@@ -95,44 +58,6 @@ __device__ __forceinline__ uint32_t mov(uint32_t v, uint32_t identity)
     return (uint32_t)__builtin_amdgcn_update_dpp((int)identity, (int)v, CTRL, ROW_MASK, 0xF, false);
 }
 }  // namespace dpp
-
-template <class Op>
-__device__ __forceinline__ uint32_t wave_reduce_bits(uint32_t v, uint32_t identity, Op op)
-{
-    v = op(v, dpp::mov<dpp::kQuadSwap1>(v, identity));
-    v = op(v, dpp::mov<dpp::kQuadSwap2>(v, identity));
-    v = op(v, dpp::mov<dpp::kRowHalfMirror>(v, identity));
-    v = op(v, dpp::mov<dpp::kRowMirror>(v, identity));
-    v = op(v, dpp::mov<dpp::kRowBcast15, 0xA>(v, identity));
-    v = op(v, dpp::mov<dpp::kRowBcast31, 0xC>(v, identity));
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
-}
-
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v)
-{
-    return wave_reduce_bits(v, 0u, [](uint32_t a, uint32_t b) { return max(a, b); });
-}
-
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v)
-{
-    return wave_reduce_bits(v, 0xFFFFFFFFu, [](uint32_t a, uint32_t b) { return min(a, b); });
-}
-
-__device__ __forceinline__ float wave_max_f32_dpp(float v)
-{
-    return __uint_as_float(wave_reduce_bits(__float_as_uint(v), __float_as_uint(-INFINITY),
-                                            [](uint32_t a, uint32_t b) {
-                                                return __float_as_uint(
-                                                    fmaxf(__uint_as_float(a), __uint_as_float(b)));
-                                            }));
-}
-
-__device__ __forceinline__ float wave_sum_f32_dpp(float v)
-{
-    return __uint_as_float(wave_reduce_bits(__float_as_uint(v), 0u, [](uint32_t a, uint32_t b) {
-        return __float_as_uint(__uint_as_float(a) + __uint_as_float(b));
-    }));
-}
 
 __device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane)
 {

@@ -32,17 +32,19 @@
 //    while the current one is multiplied from LDS (rows padded to 144 bytes,
 //    conflict-free 16-byte fragment reads). The epilogue rounds to bf16
 //    (nearest even), stages the tile in LDS and writes 16-byte row chunks.
-//    Tiles are dealt so that each XCD takes runs of consecutive tiles: a
-//    band's 128-row A slab is read into one L2.
+//    Work units (a band by up to 4 column tiles) are dealt so that each XCD
+//    takes runs of consecutive units: a band's 128-row A slab is read into
+//    one L2.
 //  * expert_return_kernel: the same GEMM in producer blocks, which after
-//    each tile release-add 1 to the band's counter; consumer blocks take
-//    tasks in order, wait (bounded) until every band of the task counts
-//    all its column tiles, then copy the task's rows to ret. One cooperative
-//    launch keeps every block resident, so no consumer waits on a producer
-//    that cannot run; a wait that exceeds its bound sets the status word
-//    and skips the copy instead of spinning on.
-#include <hip/hip_cooperative_groups.h>
-
+//    each unit release-add its column tiles to the band's count (one L2
+//    write-back per unit, which other XCDs need to see the tile). With
+//    consumer blocks, those take tasks in order, wait (bounded) until every
+//    band of the task has all its column tiles, then copy the task's rows to
+//    ret; a wait that exceeds its bound sets the status word and skips the
+//    copy instead of spinning on. Without them, the unit that completes a
+//    band counts it toward its task and the one that completes the task
+//    copies it. One cooperative launch keeps every block resident, so no
+//    consumer waits on a producer that cannot run.
 #include "device.hpp"
 #include "launch.hpp"
 
