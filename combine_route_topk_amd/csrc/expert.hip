@@ -28,9 +28,12 @@
 //  * expert_linear_kernel: a persistent grouped GEMM. Tile = 128 rows x 128
 //    output columns of one band, K-steps of 64; 256 threads as 2 x 2 waves,
 //    each wave 64 x 64 with v_mfma_f32_32x32x16_bf16 (bf16 in, fp32
-//    accumulate). The next K-step's tiles are prefetched into registers
-//    while the current one is multiplied from LDS (rows padded to 144 bytes,
-//    conflict-free 16-byte fragment reads). The epilogue rounds to bf16
+//    accumulate). Two LDS buffers: while one K-step multiplies out of one,
+//    the next step's tiles arrive in registers and are stored into the
+//    other, so a step has one barrier. Each 16-wide substep's fragments are
+//    read before the previous substep's MFMAs (rows padded to 144 bytes,
+//    conflict-free 16-byte reads). Rows past a band re-read its last row, so
+//    the loads carry no condition. The epilogue rounds to bf16
 //    (nearest even), stages the tile in LDS and writes 16-byte row chunks.
 //    Work units (a band by up to 4 column tiles) are dealt so that each XCD
 //    takes runs of consecutive units: a band's 128-row A slab is read into
@@ -56,7 +59,7 @@ constexpr int kBM = 128, kBN = 128, kBK = 64;
 constexpr int kRowBytes = kBK * 2 + 16;        // LDS row: 64 bf16 + 16 bytes of padding
 constexpr int kTileLds = kBM * kRowBytes;      // one operand tile in LDS
 constexpr int kCRowBytes = kBN * 2 + 16;       // LDS row of the staged output tile
-constexpr int kLdsBytes = 2 * kTileLds;        // A and B tiles (the output stage fits inside)
+constexpr int kLdsBytes = 4 * kTileLds;        // two buffers of A and B tiles (the output stage fits inside)
 static_assert(kBM * kCRowBytes <= kLdsBytes, "output stage must fit the operand space");
 constexpr int kTableThreads = 1024;
 constexpr int kColGroup = 4;                  // column tiles per producer work unit
@@ -253,55 +256,80 @@ __device__ void gemm_tile(const uint16_t *__restrict__ x, const uint16_t *__rest
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1), wave = tid / kWave;
     const int wm = wave >> 1, wn = wave & 1;
-    // global -> register mapping: 4 rows per thread, one 16-byte chunk of the K-step each
+    // global -> register mapping: 4 rows per thread, one 16-byte chunk of the
+    // K-step each. Rows past the band re-read its last row (a valid address;
+    // those results are never stored), so the loads carry no condition.
     const int lrow = tid >> 3, lchunk = tid & 7;
+    const u32x4 *arow[4], *brow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = lrow + 32 * i;
+        arow[i] = reinterpret_cast<const u32x4 *>(x + (int64_t)(row0 + min(r, rows - 1)) * H) + lchunk;
+        brow[i] = reinterpret_cast<const u32x4 *>(Wl + (int64_t)(n0 + r) * H) + lchunk;
+    }
     u32x4 ra[4], rb[4];
     auto load = [&](int k0) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int r = lrow + 32 * i;
-            ra[i] = r < rows ? *reinterpret_cast<const u32x4 *>(x + (int64_t)(row0 + r) * H + k0 + lchunk * 8)
-                             : u32x4{0u, 0u, 0u, 0u};
-            rb[i] = *reinterpret_cast<const u32x4 *>(Wl + (int64_t)(n0 + r) * H + k0 + lchunk * 8);
+            ra[i] = arow[i][k0 / 8];
+            rb[i] = brow[i][k0 / 8];
         }
     };
-    uint8_t *As = lds, *Bs = lds + kTileLds;
+    auto stash = [&](uint8_t *buf) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = lrow + 32 * i;
+            *reinterpret_cast<u32x4 *>(buf + r * kRowBytes + lchunk * 16) = ra[i];
+            *reinterpret_cast<u32x4 *>(buf + kTileLds + r * kRowBytes + lchunk * 16) = rb[i];
+        }
+    };
     f32x16 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             acc[i][j] = f32x16{};
+    // two LDS buffers: while one K-step multiplies out of one buffer, the next
+    // step's tile lands in registers and is stored into the other, so a step
+    // needs one barrier
     load(0);
-    for (int k0 = 0; k0 < H; k0 += kBK) {
-        __syncthreads();  // the previous step's fragment reads are done
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = lrow + 32 * i;
-            *reinterpret_cast<u32x4 *>(As + r * kRowBytes + lchunk * 16) = ra[i];
-            *reinterpret_cast<u32x4 *>(Bs + r * kRowBytes + lchunk * 16) = rb[i];
-        }
-        __syncthreads();
-        if (k0 + kBK < H)
+    stash(lds);
+    __syncthreads();
+    const int arow0 = (wm * 64 + (lane & 31)) * kRowBytes, brow0 = (wn * 64 + (lane & 31)) * kRowBytes;
+    const int khalf = 16 * (lane >> 5);  // bytes: this lane's 8 k-values of a 16-wide step
+    for (int k0 = 0, step = 0; k0 < H; k0 += kBK, ++step) {
+        const uint8_t *As = lds + (step & 1) * 2 * kTileLds, *Bs = As + kTileLds;
+        const bool more = k0 + kBK < H;
+        if (more)
             load(k0 + kBK);  // in flight while this step multiplies
+        // fragments of the next 16-wide step are read before this one's MFMAs
+        bf16x8 af[2][2], bfr[2][2];
 #pragma unroll
-        for (int kk = 0; kk < kBK; kk += 16) {
-            const int koff = (kk + 8 * (lane >> 5)) * 2;
-            bf16x8 af[2], bfr[2];
+        for (int i = 0; i < 2; ++i) {
+            af[0][i] = *reinterpret_cast<const bf16x8 *>(As + arow0 + i * 32 * kRowBytes + khalf);
+            bfr[0][i] = *reinterpret_cast<const bf16x8 *>(Bs + brow0 + i * 32 * kRowBytes + khalf);
+        }
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                af[i] = *reinterpret_cast<const bf16x8 *>(As + (wm * 64 + i * 32 + (lane & 31)) * kRowBytes + koff);
-                bfr[i] = *reinterpret_cast<const bf16x8 *>(Bs + (wn * 64 + i * 32 + (lane & 31)) * kRowBytes + koff);
+        for (int kk = 0; kk < kBK / 16; ++kk) {
+            const int cur = kk & 1, nxt = cur ^ 1;
+            if (kk + 1 < kBK / 16) {
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    af[nxt][i] = *reinterpret_cast<const bf16x8 *>(As + arow0 + i * 32 * kRowBytes + (kk + 1) * 32 + khalf);
+                    bfr[nxt][i] = *reinterpret_cast<const bf16x8 *>(Bs + brow0 + i * 32 * kRowBytes + (kk + 1) * 32 + khalf);
+                }
             }
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
         }
+        if (more)
+            stash(lds + ((step + 1) & 1) * 2 * kTileLds);
+        __syncthreads();  // the next buffer is complete; this one may be overwritten next step
     }
     // epilogue: round to bf16, stage the tile in LDS, write 16-byte chunks of rows
-    __syncthreads();
     uint16_t *Cs = reinterpret_cast<uint16_t *>(lds);
     constexpr int kCStride = kCRowBytes / 2;
 #pragma unroll
