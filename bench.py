@@ -32,6 +32,11 @@ none part of `value`:
   * the tile-signalled return: a stand-in expert GEMM on those segments whose
     tiles are returned as they finish, against the GEMM then a copy.
 
+Alongside: the spread of single-step times (a third pass with one event
+between steps) and a synthetic floor -- a device-to-device copy moving the
+step's byte count, half read and half written, timed like the step -- as
+the achievable HBM rate for the same volume.
+
 The CPU-baseline leg times the plain C oracle on the same host arrays.
 """
 
@@ -78,6 +83,8 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="time replays of a captured HIP graph of the step instead of eager launches "
                         "(on MI355X with ROCm 7 a replay costs more than four eager launches)")
+    p.add_argument("--no-floor", action="store_true",
+                   help="skip the synthetic floor (a device-to-device copy of the step's bytes)")
     p.add_argument("--no-fp8", action="store_true",
                    help="skip the FP8-payload step measurement (reported under next_rows)")
     p.add_argument("--no-tile-return", action="store_true",
@@ -481,6 +488,20 @@ def main():
                    for i, (name, _) in enumerate(calls)}
     log("per call (us): " + ", ".join(f"{n}={v * 1e3:.1f}" for n, v in per_call_ms.items()))
 
+    # pass 3: K more steps with one event between consecutive steps, for the
+    # spread of single-step times (median, p10, p90)
+    bounds = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    bounds[0].record(stream)
+    for s in range(args.steps):
+        step()
+        bounds[s + 1].record(stream)
+    torch.cuda.synchronize()
+    step_us = sorted(bounds[s].elapsed_time(bounds[s + 1]) * 1e3 for s in range(args.steps))
+    pct = lambda q: step_us[min(len(step_us) - 1, int(round(q * (len(step_us) - 1))))]
+    spread = {"p10": round(pct(0.1), 1), "p50": round(pct(0.5), 1), "p90": round(pct(0.9), 1)}
+    log("single-step us", spread)
+
     # bookkeeping from the path's own outputs (outside the timed region)
     N = int(lay["expert_offsets"][E].item())
     T_read = int((lay["pos"] >= 0).any(dim=1).sum().item())
@@ -504,6 +525,29 @@ def main():
         moe, torch, lay, send, R, E // R, H, send_rows, stream, args.warmup, args.steps)
     regroup = None if args.no_regroup or R < 2 else bench_regroup(
         moe, torch, lay, send, R, E // R, H, send_rows, stream, args.warmup, args.steps, w.name)
+
+    # synthetic floor: a device-to-device copy moving the step's byte count
+    # (half read, half written), timed like the step
+    floor = None
+    if not args.no_floor:
+        half = total // 2
+        src = torch.empty(half, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup):
+            dst.copy_(src)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(args.steps):
+            dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        floor_ms = e0.elapsed_time(e1) / args.steps
+        floor = {"bytes": 2 * half, "us": round(floor_ms * 1e3, 1),
+                 "GBps": round(2 * half / (floor_ms * 1e-3) / 1e9, 1)}
+        floor["value_frac_of_floor"] = round(gbps / floor["GBps"], 4)
+        del src, dst
+        log("synthetic floor", floor)
 
     copy_probe = None
     if args.copy_probe_mib:
@@ -548,6 +592,8 @@ def main():
         "ms_per_step_eager": round(ms_eager, 5),
         "per_call_note": "second pass of the same K steps with an event pair around every call",
         "per_call_GBps": {n: round(nbytes[n] / (per_call_ms[n] * 1e-3) / 1e9, 1) for n in nbytes},
+        "step_us_spread": spread,
+        "step_us_spread_note": "third pass of K steps with one event between consecutive steps",
         "roofline": roofline,
     }
     next_rows = {}
@@ -559,6 +605,8 @@ def main():
         next_rows["tile_signalled_return"] = tile_return
     if next_rows:
         result["next_rows"] = next_rows
+    if floor:
+        result["synthetic_floor"] = floor
     if copy_probe:
         result["copy_probe"] = copy_probe
 
