@@ -170,21 +170,69 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
         // drop every expert outside them
         const int32_t gsize = E / n_groups;
         int gid[NSLOT];
-#pragma unroll
-        for (int i = 0; i < NSLOT; ++i)
-            gid[i] = (int)(slot_id<VEC, HW>(i, gl) / (uint32_t)gsize);
         uint32_t my_gkey = 0u;
-        for (int g = 0; g < n_groups; ++g) {
-            uint32_t v = 0u;
+        if (VEC == 4 && TPW == 1 && (gsize == 16 || gsize == 32 || gsize == 64)) {
+            // Slot quad q of lane l holds experts 256q + 4l .. +3 and a group
+            // of 16, 32 or 64 divides 256, so the quad's group is
+            // q * (256 / gsize) + l / (gsize / 4), and group g's best key is
+            // the max over a segment of gsize / 4 consecutive lanes of one
+            // quad (padding keys past E are 0 and fall in groups >=
+            // n_groups). DPP steps inside 16-lane rows leave every lane of a
+            // segment with its segment's max, and one bpermute per quad
+            // hands group g's max to lane g: the values of the general loop
+            // below, with no division and no wave-wide reduction per group.
+            const int shift = gsize == 16 ? 2 : (gsize == 32 ? 3 : 4);  // log2 of lanes per group
+            const int seg = 1 << shift;
+            const int per_quad = kWave >> shift;  // groups in one quad
+#pragma unroll
+            for (int q = 0; q < NSLOT / 4; ++q) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    gid[4 * q + c] = q * per_quad + (gl >> shift);
+                auto mx = [](uint32_t a, uint32_t b) { return max(a, b); };
+                uint32_t v = mx(mx(key[4 * q], key[4 * q + 1]), mx(key[4 * q + 2], key[4 * q + 3]));
+                v = mx(v, dpp::mov<dpp::kQuadSwap1>(v, 0u));
+                v = mx(v, dpp::mov<dpp::kQuadSwap2>(v, 0u));
+                if (seg >= 8)
+                    v = mx(v, dpp::mov<dpp::kRowHalfMirror>(v, 0u));
+                if (seg >= 16)
+                    v = mx(v, dpp::mov<dpp::kRowMirror>(v, 0u));
+                // lane g of this quad's groups reads the first lane of its segment
+                const int gq = lane - q * per_quad;
+                const bool here = gq >= 0 && gq < per_quad;
+                const uint32_t got =
+                    (uint32_t)__builtin_amdgcn_ds_bpermute((here ? gq << shift : 0) << 2, (int)v);
+                my_gkey = here ? got : my_gkey;
+            }
+        } else {
 #pragma unroll
             for (int i = 0; i < NSLOT; ++i)
-                v = gid[i] == g ? max(v, key[i]) : v;
-            const uint32_t best = G::max_u32(v);
-            my_gkey = gl == g ? best : my_gkey;
+                gid[i] = (int)(slot_id<VEC, HW>(i, gl) / (uint32_t)gsize);
+            for (int g = 0; g < n_groups; ++g) {
+                uint32_t v = 0u;
+#pragma unroll
+                for (int i = 0; i < NSLOT; ++i)
+                    v = gid[i] == g ? max(v, key[i]) : v;
+                const uint32_t best = G::max_u32(v);
+                my_gkey = gl == g ? best : my_gkey;
+            }
         }
         uint64_t chosen = 0;
+        // with one token per wave and at most 16 groups every group key
+        // lies in the first 16-lane row, so a row max suffices
+        const bool row0 = TPW == 1 && n_groups <= 16;
         for (int m = 0; m < topk_groups; ++m) {
-            const uint32_t best = G::max_u32(my_gkey);
+            uint32_t best;
+            if (row0) {
+                uint32_t v = my_gkey;
+                v = max(v, dpp::mov<dpp::kQuadSwap1>(v, 0u));
+                v = max(v, dpp::mov<dpp::kQuadSwap2>(v, 0u));
+                v = max(v, dpp::mov<dpp::kRowHalfMirror>(v, 0u));
+                v = max(v, dpp::mov<dpp::kRowMirror>(v, 0u));
+                best = readlane_u32(v, 0);
+            } else {
+                best = G::max_u32(my_gkey);
+            }
             const uint64_t holders = ballot64(my_gkey == best && gl < n_groups);
             // the lowest holding lane of each token's lanes
             const uint64_t mine = TPW == 1 ? holders

@@ -407,6 +407,11 @@ GROUPED = [
     # T, E, k, n_groups, topk_groups, bias
     (32768, 512, 10, 8, 4, None),      # fine-grained shape, 8 groups of 64, at most 4
     (4096, 384, 8, 64, 4, "uniform"),  # one group per destination of 6 experts
+    (3000, 256, 8, 8, 4, "uniform"),   # groups of 32 in one 16-byte slot quad
+    (2000, 320, 8, 20, 4, "uniform"),  # groups of 16, E not a multiple of 256
+    (700, 960, 9, 30, 5, None),        # groups of 32, 4 slot quads, last one partial
+    (1500, 1024, 12, 16, 3, "uniform"),  # groups of 64, 16 slots per lane
+    (513, 192, 6, 12, 2, None),        # groups of 16, one partial slot quad
     (999, 256, 8, 32, 8, "uniform"),
     (500, 100, 7, 4, 2, None),         # E % 4 == 0 but tiny groups of 25
     (333, 70, 6, 7, 2, "uniform"),     # 4-byte route path
