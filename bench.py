@@ -33,7 +33,9 @@ none part of `value`:
     tiles are returned as they finish, against the GEMM then a copy.
 
 Alongside: the spread of single-step times (a third pass with one event
-between steps) and a synthetic floor -- a device-to-device copy moving the
+between steps), the same spread from a cold cache (a fourth pass, each step
+after a 1 GiB scratch read that evicts the Infinity Cache) and a synthetic
+floor -- a device-to-device copy moving the
 step's byte count, half read and half written, timed like the step -- as
 the achievable HBM rate for the same volume.
 
@@ -83,6 +85,8 @@ def parse():
     p.add_argument("--graph", action="store_true",
                    help="time replays of a captured HIP graph of the step instead of eager launches "
                         "(on MI355X with ROCm 7 a replay costs more than four eager launches)")
+    p.add_argument("--no-cold", action="store_true",
+                   help="skip the cold-cache pass (each step after a 1 GiB scratch read)")
     p.add_argument("--no-floor", action="store_true",
                    help="skip the synthetic floor (a device-to-device copy of the step's bytes)")
     p.add_argument("--no-fp8", action="store_true",
@@ -279,6 +283,7 @@ def bench_fp8(moe, torch, calls, lay, x, wt, sh, res, T, H, E, k, send_rows, nby
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+CONSUMER_COUNTS = (16, 24, 32, 0)   # dedicated consumer blocks tried by the tile-signalled return
 
 
 def bench_tile_return(moe, torch, lay, send, S, El, H, rows, stream, warmup, steps, seed=0):
@@ -287,8 +292,8 @@ def bench_tile_return(moe, torch, lay, send, S, El, H, rows, stream, warmup, ste
     H x H linear map per local expert, MFMA bf16), and the results return to
     the sources' buffer. Timed: the GEMM alone, the GEMM then a copy of y to
     ret (the return starting after the GEMM), and the signalled launch with
-    32 dedicated consumer blocks and with none (producers return their own
-    tasks). FLOPs per GEMM: 2 * N * H * H."""
+    16, 24 and 32 dedicated consumer blocks (of one block per CU) and with
+    none (producers return their own tasks). FLOPs per GEMM: 2 * N * H * H."""
     dev = send.device
     cnt = lay["expert_counts"].view(S, El)
     W = torch.from_numpy(synthetic.make_expert_weights(El, H, H, seed).view(np.int16)).to(dev).view(torch.bfloat16)
@@ -311,7 +316,7 @@ def bench_tile_return(moe, torch, lay, send, S, El, H, rows, stream, warmup, ste
     gemm = lambda: moe.moe_expert_linear(send, cnt, W, y=y, workspace=ws)
     us = {"gemm": timed(gemm), "gemm_then_copy": timed(lambda: (gemm(), ret.copy_(y)))}
     status = {}
-    for consumers in (32, 0):
+    for consumers in CONSUMER_COUNTS:
         key = f"signalled_consumers_{consumers}"
         us[key] = timed(lambda: moe.moe_expert_linear_return(send, cnt, W, 0, consumers, 2, y=y, ret=ret,
                                                              workspace=ws))
@@ -323,7 +328,7 @@ def bench_tile_return(moe, torch, lay, send, S, El, H, rows, stream, warmup, ste
         raise RuntimeError("returned rows differ from the expert output")
     flops = 2.0 * N * H * H
     tflops = flops / (us["gemm"] * 1e-6) / 1e12
-    best = min(("signalled_consumers_32", "signalled_consumers_0"), key=lambda k: us[k])
+    best = min((k for k in us if k.startswith("signalled_")), key=lambda k: us[k])
     out = {"rows": N, "sources": S, "local_experts": El, "H": H,
            "per_call_us": {k: round(v, 1) for k, v in us.items()},
            "signalled_vs_sequential": round(us["gemm_then_copy"] / us[best], 3),
@@ -502,6 +507,29 @@ def main():
     spread = {"p10": round(pct(0.1), 1), "p50": round(pct(0.5), 1), "p90": round(pct(0.9), 1)}
     log("single-step us", spread)
 
+    # pass 4: K more steps from a cold cache -- before each, outside its
+    # event pair, a read of a 1 GiB scratch buffer pushes the step's arrays
+    # out of the 256 MB Infinity Cache. A read, not a write: dirty scratch
+    # lines left in the cache would be written back during the step and
+    # charged to it (36 us on fine_grained, measured).
+    cold = None
+    if not args.no_cold:
+        scratch = torch.zeros(1 << 28, dtype=torch.int32, device=dev)
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for s in range(args.steps):
+            torch.amax(scratch)
+            cev[s][0].record(stream)
+            step()
+            cev[s][1].record(stream)
+        torch.cuda.synchronize()
+        cold_us = sorted(a.elapsed_time(b) * 1e3 for a, b in cev)
+        cp = lambda q: cold_us[min(len(cold_us) - 1, int(round(q * (len(cold_us) - 1))))]
+        cold = {"p10": round(cp(0.1), 1), "p50": round(cp(0.5), 1), "p90": round(cp(0.9), 1)}
+        del scratch
+        log("cold-cache single-step us", cold)
+
     # bookkeeping from the path's own outputs (outside the timed region)
     N = int(lay["expert_offsets"][E].item())
     T_read = int((lay["pos"] >= 0).any(dim=1).sum().item())
@@ -594,6 +622,9 @@ def main():
         "per_call_GBps": {n: round(nbytes[n] / (per_call_ms[n] * 1e-3) / 1e9, 1) for n in nbytes},
         "step_us_spread": spread,
         "step_us_spread_note": "third pass of K steps with one event between consecutive steps",
+        "step_us_cold": cold,
+        "step_us_cold_note": ("fourth pass of K steps, each after a read of a 1 GiB scratch buffer "
+                              "(outside its event pair) that evicts the 256 MB Infinity Cache"),
         "roofline": roofline,
     }
     next_rows = {}

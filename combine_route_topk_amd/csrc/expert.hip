@@ -25,21 +25,20 @@
 //    self last -- and the consumer tasks (up to band_group bands of one
 //    source). It also clears the band flags and the status word, with
 //    ordinary stores, so a call needs no memset.
-//  * expert_linear_kernel: a persistent grouped GEMM. Tile = 128 rows x 128
-//    output columns of one band, K-steps of 64; 256 threads as 2 x 2 waves,
-//    each wave 64 x 64 with v_mfma_f32_32x32x16_bf16 (bf16 in, fp32
-//    accumulate). Two LDS buffers: while one K-step multiplies out of one,
-//    the next step's tiles arrive in registers and are stored into the
-//    other, so a step has one barrier. Each 16-wide substep's fragments are
-//    read before the previous substep's MFMAs (rows padded to 144 bytes,
-//    conflict-free 16-byte reads). Rows past a band re-read its last row, so
-//    the loads carry no condition. The epilogue rounds to bf16
-//    (nearest even), stages the tile in LDS and writes 16-byte row chunks.
-//    Work units (a band by up to 4 column tiles) are dealt so that each XCD
-//    takes runs of consecutive units: a band's 128-row A slab is read into
-//    one L2.
+//  * expert_linear_kernel: a persistent grouped GEMM, one block per CU. Tile
+//    = 128 rows (one band) x 512 output columns, K-steps of 32; 4 waves,
+//    each 128 x 128 of the tile with v_mfma_f32_32x32x16_bf16 (bf16 in,
+//    fp32 accumulate, all 256 AGPRs). Operands go straight from memory to LDS
+//    (buffer loads with an LDS destination) through four 40 KiB stages, so
+//    a K-step's loads are issued three steps ahead and hold no registers;
+//    the next step's first fragments are read while this step multiplies.
+//    LDS rows carry no padding: a chunk permutation keeps the fragment reads
+//    conflict-free. The epilogue rounds to bf16 (nearest even), stages the
+//    tile in LDS and writes 16-byte row chunks. Work units (a band by one
+//    column tile) are dealt so that each XCD takes runs of consecutive
+//    units: a band's 128-row A slab is read into one L2.
 //  * expert_return_kernel: the same GEMM in producer blocks, which after
-//    each unit release-add its column tiles to the band's count (one L2
+//    each unit release-add one to the band's count of column tiles (one L2
 //    write-back per unit, which other XCDs need to see the tile). With
 //    consumer blocks, those take tasks in order, wait (bounded) until every
 //    band of the task has all its column tiles, then copy the task's rows to
@@ -55,15 +54,24 @@ namespace moe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBM = 128, kBN = 128, kBK = 64;
-constexpr int kRowBytes = kBK * 2 + 16;        // LDS row: 64 bf16 + 16 bytes of padding
-constexpr int kTileLds = kBM * kRowBytes;      // one operand tile in LDS
-constexpr int kCRowBytes = kBN * 2 + 16;       // LDS row of the staged output tile
-constexpr int kLdsBytes = 4 * kTileLds;        // two buffers of A and B tiles (the output stage fits inside)
+// GEMM tile: 128 rows (one band) x 512 output columns, K-steps of 32; each of
+// the 4 waves owns 128 x 128 of the tile (16 fp32 accumulators of 32 x 32).
+constexpr int kBM = 128, kBN = 512, kBK = 32, kStages = 4;
+constexpr int kRowB = kBK * 2;                        // 64-byte LDS rows, no padding (swizzled)
+constexpr int kABytes = kBM * kRowB;                  // 8 KiB: the band's rows of one K-step
+constexpr int kBBytes = kBN * kRowB;                  // 32 KiB: the tile's W rows of one K-step
+constexpr int kStageBytes = kABytes + kBBytes;
+constexpr int kLdsBytes = kStages * kStageBytes;      // 160 KiB: all of a CU's LDS, one block per CU
+constexpr int kCRowBytes = kBN * 2 + 16;              // LDS row of the staged output tile
 static_assert(kBM * kCRowBytes <= kLdsBytes, "output stage must fit the operand space");
+constexpr int kFillA = kABytes / 1024 / 4, kFillB = kBBytes / 1024 / 4;  // 1 KiB fills per wave per stage
+constexpr int kFill = kFillA + kFillB;
 constexpr int kTableThreads = 1024;
-constexpr int kColGroup = 4;                  // column tiles per producer work unit
 constexpr int kSpinLimit = 1 << 21;            // polls before a wait gives up (about 1 s)
+
+// word 3 of a buffer resource for plain byte-addressed loads (32-bit data
+// format, as raw buffer loads on this architecture require)
+constexpr int kBufferFlags = 0x00020000;
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -247,109 +255,202 @@ __device__ __forceinline__ Band band_info(const LinearWs &ws, const int32_t *cnt
     return b;
 }
 
-// One 128 x 128 output tile: y[row0 .. row0+rows)[n0 .. n0+128) =
-// x[rows] . W[l][n0 .. n0+128)^T, accumulated over K = H in fp32.
-__device__ void gemm_tile(const uint16_t *__restrict__ x, const uint16_t *__restrict__ Wl,
-                          int32_t row0, int32_t rows, int32_t n0, int32_t H, int32_t H_out,
-                          uint16_t *__restrict__ y, uint8_t *lds)
+// Position of 16-byte chunk c of 64-byte LDS row i: c ^ swz(i & 15). A 16-byte
+// read of one chunk from 16 consecutive rows (or from 8) then touches
+// distinct banks, with no padding.
+__device__ __forceinline__ int swz(int i) { return ((i >> 1) & 3) ^ (((i >> 3) & 1) * 3); }
+
+// wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void wait_vmem()
 {
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1), wave = tid / kWave;
-    const int wm = wave >> 1, wn = wave & 1;
-    // global -> register mapping: 4 rows per thread, one 16-byte chunk of the
-    // K-step each. Rows past the band re-read its last row (a valid address;
-    // those results are never stored), so the loads carry no condition.
-    const int lrow = tid >> 3, lchunk = tid & 7;
-    const u32x4 *arow[4], *brow[4];
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ bf16x8 frag(const uint8_t *__restrict__ base, int row, int blk, int koff)
+{
+    return *reinterpret_cast<const bf16x8 *>(base + row + blk * 32 * kRowB + koff);
+}
+
+// Start the loads of one stage: x's band rows and the tile's W rows for the
+// K-step at byte offset kb go straight to LDS (buffer loads with an LDS
+// destination, 1 KiB per instruction and wave: 16 rows x 64 bytes).
+__device__ __forceinline__ void fill_stage(uint8_t *__restrict__ fill, __amdgpu_buffer_rsrc_t ra,
+                                           __amdgpu_buffer_rsrc_t rb, int kb,
+                                           const uint32_t (&aoff)[kFillA], const uint32_t (&boff)[kFillB],
+                                           int wave)
+{
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = lrow + 32 * i;
-        arow[i] = reinterpret_cast<const u32x4 *>(x + (int64_t)(row0 + min(r, rows - 1)) * H) + lchunk;
-        brow[i] = reinterpret_cast<const u32x4 *>(Wl + (int64_t)(n0 + r) * H) + lchunk;
+    for (int i = 0; i < kFillA; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, fill + (i * 4 + wave) * 1024, 16, aoff[i], kb, 0, 0);
+#pragma unroll
+    for (int i = 0; i < kFillB; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, fill + kABytes + (i * 4 + wave) * 1024, 16, boff[i], kb, 0, 0);
+}
+
+__device__ __forceinline__ void first_frags(const uint8_t *__restrict__ cur, int arow, int brow, int koff0,
+                                            bf16x8 (&f0)[8])
+{
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+        f0[q] = q < 4 ? frag(cur, arow, q, koff0) : frag(cur + kABytes, brow, q - 4, koff0);
+}
+
+// One K-step of 32: multiply the first 16 of stage `cur` (fragments f0, read
+// during the previous step) while reading its second 16 into f1, then
+// multiply those while reading the first 16 of stage `nxt` into f0 (MORE);
+// with LOAD, the fill of stage `fill` is spread over the first half. The
+// groups are pinned in this order, so LDS reads and fills overlap the
+// MFMAs. The stage pointers are restrict-qualified: the compiler then knows
+// that reads of one stage do not depend on the fill of another and leaves
+// the waits to the caller's explicit ones.
+template <bool LOAD, bool MORE>
+__device__ __forceinline__ void kstep(const uint8_t *__restrict__ cur, const uint8_t *__restrict__ nxt,
+                                      uint8_t *__restrict__ fill, __amdgpu_buffer_rsrc_t ra,
+                                      __amdgpu_buffer_rsrc_t rb, int kb, const uint32_t (&aoff)[kFillA],
+                                      const uint32_t (&boff)[kFillB], int wave, int arow, int brow,
+                                      const int (&koff)[2], bf16x8 (&f0)[8], bf16x8 (&f1)[8],
+                                      f32x16 (&acc)[4][4])
+{
+    static_assert(kFillA + kFillB == 10, "the fill schedule below spreads 10 loads over 8 groups");
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        if (LOAD) {
+            if (q < kFillA)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, fill + (q * 4 + wave) * 1024, 16, aoff[q], kb, 0, 0);
+            else
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, fill + kABytes + ((q - kFillA) * 4 + wave) * 1024,
+                                                         16, boff[q - kFillA], kb, 0, 0);
+            if (q < 2)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, fill + kABytes + ((6 + q) * 4 + wave) * 1024, 16,
+                                                         boff[6 + q], kb, 0, 0);
+        }
+        f1[q] = q < 4 ? frag(cur, arow, q, koff[1]) : frag(cur + kABytes, brow, q - 4, koff[1]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int i = q >> 1, j = (q & 1) * 2;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[i], f0[4 + j], acc[i][j], 0, 0, 0);
+        acc[i][j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f0[i], f0[5 + j], acc[i][j + 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
     }
-    u32x4 ra[4], rb[4];
-    auto load = [&](int k0) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            ra[i] = arow[i][k0 / 8];
-            rb[i] = brow[i][k0 / 8];
-        }
-    };
-    auto stash = [&](uint8_t *buf) {
+    for (int q = 0; q < 8; ++q) {
+        if (MORE)  // f0[q] is free: the first half's MFMAs have read it
+            f0[q] = q < 4 ? frag(nxt, arow, q, koff[0]) : frag(nxt + kABytes, brow, q - 4, koff[0]);
+        __builtin_amdgcn_sched_barrier(0);
+        const int i = q >> 1, j = (q & 1) * 2;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[i], f1[4 + j], acc[i][j], 0, 0, 0);
+        acc[i][j + 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f1[i], f1[5 + j], acc[i][j + 1], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// One 128 x 512 output tile: y[row0 .. row0+rows)[n0 .. n0+512) =
+// x[rows] . W[l][n0 .. n0+512)^T, accumulated over K = H in fp32, columns at
+// or past H_out not stored. The K-steps stream through four LDS stages: at
+// the top of step s, stage s + 1 is complete (every wave waits for its own
+// fills, then a barrier), so step s reads the first fragments of stage
+// s + 1 while it multiplies stage s, and fills stage s + 3. Rows past the
+// band re-read its last row and W rows past H_out its last row, so no load
+// carries a condition; the buffer ranges cover exactly the band's rows and
+// the tile's W rows.
+__device__ __forceinline__ void gemm_tile(const uint16_t *__restrict__ x, const uint16_t *__restrict__ Wl,
+                                          int32_t row0, int32_t rows, int32_t n0, int32_t H, int32_t H_out,
+                                          uint16_t *__restrict__ y, uint8_t *lds)
+{
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    // the tile is the same for every lane; saying so keeps the buffer
+    // resources in scalar registers (no per-lane loop around each load)
+    row0 = __builtin_amdgcn_readfirstlane(row0);
+    rows = __builtin_amdgcn_readfirstlane(rows);
+    n0 = __builtin_amdgcn_readfirstlane(n0);
+    const int ncols = min(kBN, H_out - n0);
+    // fill mapping: lane L of an instruction writes row L / 4, position L % 4,
+    // which holds chunk position ^ swz(row)
+    const int lr = lane >> 2, gc = (lane & 3) ^ swz(lr);
+    uint32_t aoff[kFillA], boff[kFillB];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = lrow + 32 * i;
-            *reinterpret_cast<u32x4 *>(buf + r * kRowBytes + lchunk * 16) = ra[i];
-            *reinterpret_cast<u32x4 *>(buf + kTileLds + r * kRowBytes + lchunk * 16) = rb[i];
-        }
-    };
-    f32x16 acc[2][2];
+    for (int i = 0; i < kFillA; ++i)
+        aoff[i] = (uint32_t)min((i * 4 + wave) * 16 + lr, rows - 1) * (uint32_t)H * 2u + gc * 16;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kFillB; ++i)
+        boff[i] = (uint32_t)min((i * 4 + wave) * 16 + lr, ncols - 1) * (uint32_t)H * 2u + gc * 16;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(x + (int64_t)row0 * H), 0, rows * H * 2, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(Wl + (int64_t)n0 * H), 0, ncols * H * 2, kBufferFlags);
+    f32x16 acc[4][4];
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
             acc[i][j] = f32x16{};
-    // two LDS buffers: while one K-step multiplies out of one buffer, the next
-    // step's tile lands in registers and is stored into the other, so a step
-    // needs one barrier
-    load(0);
-    stash(lds);
+    // fragment reads: row lane % 32 of each 32-row block, chunk 2 kk + lane / 32
+    const int hi = lane >> 5, sw = swz(lane & 15);
+    const int arow = (lane & 31) * kRowB, brow = (wave * 128 + (lane & 31)) * kRowB;
+    const int koff[2] = {(hi ^ sw) << 4, ((2 + hi) ^ sw) << 4};
+    const int nsteps = H / kBK;
+#pragma unroll
+    for (int st = 0; st < kStages - 1; ++st)
+        if (st < nsteps)
+            fill_stage(lds + st * kStageBytes, ra, rb, st * kBK * 2, aoff, boff, wave);
+    if (nsteps > 2)
+        wait_vmem<kFill>();
+    else
+        wait_vmem<0>();
     __syncthreads();
-    const int arow0 = (wm * 64 + (lane & 31)) * kRowBytes, brow0 = (wn * 64 + (lane & 31)) * kRowBytes;
-    const int khalf = 16 * (lane >> 5);  // bytes: this lane's 8 k-values of a 16-wide step
-    for (int k0 = 0, step = 0; k0 < H; k0 += kBK, ++step) {
-        const uint8_t *As = lds + (step & 1) * 2 * kTileLds, *Bs = As + kTileLds;
-        const bool more = k0 + kBK < H;
-        if (more)
-            load(k0 + kBK);  // in flight while this step multiplies
-        // fragments of the next 16-wide step are read before this one's MFMAs
-        bf16x8 af[2][2], bfr[2][2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            af[0][i] = *reinterpret_cast<const bf16x8 *>(As + arow0 + i * 32 * kRowBytes + khalf);
-            bfr[0][i] = *reinterpret_cast<const bf16x8 *>(Bs + brow0 + i * 32 * kRowBytes + khalf);
-        }
-#pragma unroll
-        for (int kk = 0; kk < kBK / 16; ++kk) {
-            const int cur = kk & 1, nxt = cur ^ 1;
-            if (kk + 1 < kBK / 16) {
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    af[nxt][i] = *reinterpret_cast<const bf16x8 *>(As + arow0 + i * 32 * kRowBytes + (kk + 1) * 32 + khalf);
-                    bfr[nxt][i] = *reinterpret_cast<const bf16x8 *>(Bs + brow0 + i * 32 * kRowBytes + (kk + 1) * 32 + khalf);
-                }
-            }
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j], 0, 0, 0);
-        }
-        if (more)
-            stash(lds + ((step + 1) & 1) * 2 * kTileLds);
-        __syncthreads();  // the next buffer is complete; this one may be overwritten next step
+    bf16x8 f0[8], f1[8];
+    first_frags(lds, arow, brow, koff[0], f0);
+    // top of step s > 0: stage s + 1 complete (only stage s + 2 may be in
+    // flight), then a barrier so every wave's part of it is in LDS and every
+    // wave is done with the stage the next fill overwrites
+    auto top = [&](int st) {
+        if (st == 0)
+            return;
+        if (st + 2 < nsteps)
+            wait_vmem<kFill>();
+        else
+            wait_vmem<0>();
+        asm volatile("s_barrier" ::: "memory");
+    };
+#define MOE_KSTEP(L, M)                                                                                   \
+    kstep<L, M>(lds + (st % kStages) * kStageBytes, lds + ((st + 1) % kStages) * kStageBytes,           \
+                lds + ((st + kStages - 1) % kStages) * kStageBytes, ra, rb, (st + kStages - 1) * kBK * 2, \
+                aoff, boff, wave, arow, brow, koff, f0, f1, acc)
+    int st = 0;
+    for (; st + kStages - 1 < nsteps; ++st) {
+        top(st);
+        MOE_KSTEP(true, true);
     }
+    for (; st + 1 < nsteps; ++st) {
+        top(st);
+        MOE_KSTEP(false, true);
+    }
+    top(st);
+    MOE_KSTEP(false, false);
+#undef MOE_KSTEP
+    __syncthreads();  // every wave is done with the stages
     // epilogue: round to bf16, stage the tile in LDS, write 16-byte chunks of rows
     uint16_t *Cs = reinterpret_cast<uint16_t *>(lds);
     constexpr int kCStride = kCRowBytes / 2;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int r = 0; r < 16; r += 2) {
                 // accumulator r holds row 8(r/4) + 4(lane/32) + r%4, column lane%32
-                const int row = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
-                const int col = wn * 64 + j * 32 + (lane & 31);
+                const int row = i * 32 + 8 * (r >> 2) + 4 * hi + (r & 3);
+                const int col = wave * 128 + j * 32 + (lane & 31);
                 const uint32_t p = pack_bf16x2(acc[i][j][r], acc[i][j][r + 1]);
                 Cs[row * kCStride + col] = (uint16_t)(p & 0xFFFFu);
                 Cs[(row + 1) * kCStride + col] = (uint16_t)(p >> 16);
             }
     __syncthreads();
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int r = (tid >> 4) + 16 * i, chunk = tid & 15;
-        if (r < rows)
+#pragma unroll 8
+    for (int i = 0; i < kBM * kBN / 8 / kThreads; ++i) {
+        const int r = (tid >> 6) + 4 * i, chunk = tid & 63;
+        if (r < rows && chunk * 8 < ncols)
             *reinterpret_cast<u32x4 *>(y + (int64_t)(row0 + r) * H_out + n0 + chunk * 8) =
                 *reinterpret_cast<const u32x4 *>(lds + r * kCRowBytes + chunk * 16);
     }
@@ -379,19 +480,41 @@ __device__ void return_rows(const LinearWs &ws, const int32_t *cnt, int32_t S, i
     const int64_t n16 = (r1 - r0) * C16;
     const u32x4 *src = reinterpret_cast<const u32x4 *>(y) + r0 * C16;
     u32x4 *dst = reinterpret_cast<u32x4 *>(ret) + r0 * C16;
-    // whole chunks keep 8 loads in flight per thread (32 KiB per block): no
-    // per-load condition, which would make each load wait for the last
-    constexpr int kInFlight = 8;
+    // whole chunks of 16 loads per thread (64 KiB per block), software-
+    // pipelined: chunk c + 1 is loaded before chunk c is stored, so a wait for
+    // a chunk's loads never includes the stores issued after them, and two
+    // chunks (128 KiB per block) are in flight -- a copy by few blocks is
+    // bound by bytes in flight over memory latency. No per-load condition,
+    // which would make each load wait for the last. The registers are there
+    // anyway: the kernel is sized for its GEMM.
+    constexpr int kInFlight = 16;
     constexpr int64_t kChunk = (int64_t)kThreads * kInFlight;
     const int64_t full = n16 / kChunk * kChunk;
-    for (int64_t base = threadIdx.x; base < full; base += kChunk) {
-        u32x4 v[kInFlight];
+    u32x4 va[kInFlight], vb[kInFlight];
+    auto load = [&](u32x4 (&v)[kInFlight], int64_t base) {
 #pragma unroll
         for (int u = 0; u < kInFlight; ++u)
             v[u] = load_stream(src + base + u * kThreads);
+    };
+    auto store = [&](const u32x4 (&v)[kInFlight], int64_t base) {
 #pragma unroll
         for (int u = 0; u < kInFlight; ++u)
             store_stream(dst + base + u * kThreads, v[u]);
+    };
+    int64_t base = threadIdx.x;
+    if (base < full)
+        load(va, base);
+    while (base < full) {
+        if (base + kChunk < full)
+            load(vb, base + kChunk);
+        store(va, base);
+        base += kChunk;
+        if (base >= full)
+            break;
+        if (base + kChunk < full)
+            load(va, base + kChunk);
+        store(vb, base);
+        base += kChunk;
     }
     for (int64_t i = full + threadIdx.x; i < n16; i += kThreads)
         store_stream(dst + i, load_stream(src + i));
@@ -417,20 +540,18 @@ __device__ void produce(const uint16_t *__restrict__ x, const int32_t *__restric
                         bool inline_return, int32_t band_group, uint16_t *__restrict__ ret,
                         int32_t *copy_task, uint8_t *lds)
 {
-    // a work unit is one band by up to kColGroup column tiles; it is released
-    // once (one L2 write-back per unit instead of per tile)
-    const int32_t nct = H_out / kBN;
-    const int32_t groups = (nct + kColGroup - 1) / kColGroup;
-    const int64_t n_units = (int64_t)ws.counts[0] * groups;
+    // a work unit is one band by one column tile; it is released once (one L2
+    // write-back per 512 output columns)
+    const int32_t nct = (H_out + kBN - 1) / kBN;
+    const int64_t n_units = (int64_t)ws.counts[0] * nct;
     for (int64_t step = 0; step * n_slots < n_units; ++step) {
         const int64_t u = dealt_tile(step, slot, n_slots);
         if (u >= n_units)
             continue;
-        const int32_t band = (int32_t)(u / groups), g = (int32_t)(u % groups);
+        const int32_t band = (int32_t)(u / nct), ct = (int32_t)(u % nct);
         const Band b = band_info(ws, cnt, S, El, self_rank, band);
-        const int32_t ct1 = min(nct, (g + 1) * kColGroup);
-        for (int32_t ct = g * kColGroup; ct < ct1; ++ct)
-            gemm_tile(x, W + (int64_t)b.l * H_out * H, b.row0, b.rows, ct * kBN, H, H_out, y, lds);
+        const int32_t l = __builtin_amdgcn_readfirstlane(b.l);  // the same in every lane
+        gemm_tile(x, W + (int64_t)l * H_out * H, b.row0, b.rows, ct * kBN, H, H_out, y, lds);
         if (signal) {
             // each thread's stores complete to its L2 (a workgroup-scope release is
             // a wait, no cache maintenance); then one agent-scope release by thread 0
@@ -438,7 +559,7 @@ __device__ void produce(const uint16_t *__restrict__ x, const int32_t *__restric
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
             __syncthreads();
             if (threadIdx.x == 0) {
-                const int32_t add = ct1 - g * kColGroup;
+                const int32_t add = 1;
                 int32_t task = -1;
                 if (!inline_return) {
                     __hip_atomic_fetch_add(ws.flags + band, add, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
@@ -460,9 +581,11 @@ __device__ void produce(const uint16_t *__restrict__ x, const int32_t *__restric
                 *copy_task = task;
             }
             __syncthreads();
-            if (inline_return && *copy_task >= 0) {
+            const int32_t task = *copy_task;
+            __syncthreads();  // the word lives in the tile's LDS, which the next tile's loads reuse
+            if (inline_return && task >= 0) {
                 int32_t b0, b1;
-                task_bands(ws, S, El, band_group, *copy_task, &b0, &b1);
+                task_bands(ws, S, El, band_group, task, &b0, &b1);
                 return_rows(ws, cnt, S, El, self_rank, H_out, b0, b1, y, ret);
             }
         }
@@ -487,7 +610,10 @@ __global__ __launch_bounds__(kThreads) void expert_return_kernel(
     int32_t consumers, int32_t *__restrict__ ws_base)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
-    __shared__ int32_t task_ok;
+    // the block's broadcast word shares the first bytes of the tile memory:
+    // it is written only between tiles (producers) or by blocks that run no
+    // tile (consumers)
+    int32_t &task_ok = *reinterpret_cast<int32_t *>(lds);
     const LinearWs ws = linear_ws(ws_base, S, El);
     const int32_t producers = (int32_t)gridDim.x - consumers;
     if ((int32_t)blockIdx.x < producers) {
@@ -496,7 +622,7 @@ __global__ __launch_bounds__(kThreads) void expert_return_kernel(
         return;
     }
     // consumer: tasks c, c + consumers, ... in remote-first order
-    const int32_t nct = H_out / kBN;
+    const int32_t nct = (H_out + kBN - 1) / kBN;
     const int32_t n_tasks = ws.counts[1];
     for (int32_t task = (int32_t)blockIdx.x - producers; task < n_tasks; task += consumers) {
         int32_t b0, b1;
@@ -575,7 +701,7 @@ hipError_t launch_expert_linear(const uint16_t *recv, const int32_t *cnt, int32_
     if ((err = resident_blocks(reinterpret_cast<const void *>(expert_linear_kernel), g_linear_slots,
                                &slots)) != hipSuccess)
         return err;
-    const int64_t tiles = max_bands(S, El, max_rows) * (H_out / kBN);
+    const int64_t tiles = max_bands(S, El, max_rows) * ((H_out + kBN - 1) / kBN);
     const int grid = (int)(tiles < slots ? tiles : slots);
     hipLaunchKernelGGL(expert_linear_kernel, dim3(grid), dim3(kThreads), 0, stream, recv, cnt, S,
                        El, S - 1, H, H_out, W, y, workspace);

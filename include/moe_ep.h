@@ -386,8 +386,9 @@ moe_status_t moe_recv_ungroup(const uint16_t *grouped, const int32_t *recv_pos,
  *   y[i][o] = bf16( sum_h recv[i][h] * W[l][o][h] )
  * accumulated in fp32 (MFMA) and rounded once, to nearest even, for every
  * row i < N = sum of the counts (rows past N are not written). Tiles are
- * 128 rows of one (source, expert) block by 128 output columns, so every
- * tile goes back to exactly one source.
+ * 128 rows of one (source, expert) block by 512 output columns (the last
+ * narrower when H_out % 512 != 0), so every tile goes back to exactly one
+ * source.
  *
  * Limits: as moe_recv_regroup_layout for S and E_l; H % 64 == 0,
  * H_out % 128 == 0, both <= 65536; max_rows < 2^31. Buffers 16-byte
@@ -418,10 +419,10 @@ moe_status_t moe_expert_linear(const uint16_t *recv, const int32_t *recv_counts,
  *
  * One cooperative launch of moe_expert_return_slots() blocks, all resident.
  *   - Work units (a band -- the 128-row tile of one (source, expert) block --
- *     by up to 4 column tiles) go in remote-first order: sources
+ *     by one 512-column tile) go in remote-first order: sources
  *     self_rank+1, self_rank+2, ... (mod S), self_rank last.
- *   - After each unit a producer release-adds its column tiles to the
- *     band's count.
+ *   - After each unit a producer release-adds one to the band's count of
+ *     column tiles.
  *   - A task is up to band_group consecutive bands of one source: one
  *     contiguous copy of rows from y to ret.
  * consumer_blocks > 0: that many blocks only return rows. Each takes tasks
