@@ -252,6 +252,9 @@ SHAPES = [
     (513, 16, 64, 8, 8, 70),      # 4104 assignments: the tiled layout, capacity
     (20000, 16, 64, 4, 8, 900),   # tiled layout, capacity, several tiles
     (1000, 32, 600, 4, 6, 50),    # E > 512 takes the tiled layout at any size
+    (16, 65536, 16, 2, 4, -1),    # largest H: 16 slabs of 4096 values per row
+    (262144, 8, 64, 8, 8, -1),    # 2^21 assignments: 128 tiles of 16384 (the tile grows past the cap)
+    (32768, 8, 1024, 32, 64, -1),  # 2^20 assignments at the largest E and k (8 waves per rank block)
 ]
 
 
