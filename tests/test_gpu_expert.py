@@ -87,6 +87,8 @@ CASES = [  # (S, E_l, max count, H, H_out, seed)
     (8, 1, 40, 512, 384, 2),
     (2, 8, 1000, 128, 256, 3),     # long blocks, several bands each
     (16, 6, 90, 7168 // 8, 256, 4),
+    (4, 2, 200, 256, 640, 5),      # a full 512-column tile, then a 128-column one
+    (2, 3, 300, 192, 1024, 6),     # two full column tiles; 6 K-steps
 ]
 
 
@@ -110,21 +112,23 @@ def test_expert_linear_small(moe, case):
     assert np.all(yb[N:] == CANARY), "rows past N written"
 
 
-RETURN_CASES = [  # (consumers, band_group, self_rank); 0 consumers = producers return
-    (0, 1, 0),
-    (0, 3, 2),
-    (1, 1, 0),
-    (8, 4, 3),
-    (64, 2, 1),
-    (4, 64, 2),
+RETURN_CASES = [  # (consumers, band_group, self_rank, H_out); 0 consumers = producers return
+    (0, 1, 0, 256),
+    (0, 3, 2, 256),
+    (1, 1, 0, 256),
+    (8, 4, 3, 256),
+    (64, 2, 1, 256),
+    (4, 64, 2, 256),
+    (16, 2, 1, 1152),              # three column tiles per band, the last partial
+    (0, 2, 3, 1152),
 ]
 
 
 @pytest.mark.parametrize("rc", RETURN_CASES, ids=[str(c) for c in RETURN_CASES])
 def test_signalled_return_matches_plain(moe, rc):
-    consumers, group, self_rank = rc
+    consumers, group, self_rank, H_out = rc
     r = np.random.default_rng(10 + consumers)
-    S, El, H, H_out = 4, 3, 256, 256
+    S, El, H = 4, 3, 256
     cnt = r.integers(0, 400, size=(S, El)).astype(np.int32)
     cnt[1, :] = 0                               # a source with nothing to return
     N = int(cnt.sum())
