@@ -261,9 +261,13 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
     const int b = blockIdx.x;
 
     // totals and this tile's prefix, straight from the tile histograms.
-    // Thread tid owns expert e = tid % E and tiles g, g + G, g + 2G, ...
-    // (g = tid / E, G = threads per expert), with 16 loads in flight; the
-    // G partial sums per expert meet in LDS through integer atomics.
+    // Thread tid owns a column (one expert, or with E % 4 == 0 four
+    // consecutive experts read as one 16-byte word) and tiles g, g + G,
+    // g + 2G, ... (G = threads per column), with 16 loads in flight; at
+    // fine_grained (E = 512, 128 tiles) that is every tile in one batch.
+    // The G partial sums per expert meet in LDS through integer atomics.
+    // Loads read a clamped tile and the sum drops what is past the last
+    // one, so no load carries a condition.
     for (int e = tid; e < E; e += kRankThreads) {
         cnt[e] = 0;
         base[e] = 0;
@@ -272,26 +276,62 @@ __global__ __launch_bounds__(kRankThreads) void layout_rank_kernel(
         wh[i] = 0;
     __syncthreads();
     constexpr int kHistBatch = 16;
-    const int G = E <= kRankThreads ? kRankThreads / E : 1;
-    for (int col = tid; col < G * E; col += kRankThreads) {
-        const int e = col % E;
-        const int g = col / E;
-        int32_t total = 0, before = 0;
-        for (int t0 = g; t0 < B; t0 += G * kHistBatch) {
-            int32_t h[kHistBatch];
+    // threads per column: the fewest that still take every tile in one batch
+    // (fewer threads adding into each LDS word), at most what the block holds
+    const int per_batch = (B + kHistBatch - 1) / kHistBatch;
+    if (E % 4 == 0) {
+        typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+        const i32x4 *hist4 = reinterpret_cast<const i32x4 *>(tile_hist);
+        const int EQ = E / 4;
+        const int G = max(1, min(EQ <= kRankThreads ? kRankThreads / EQ : 1, per_batch));
+        for (int col = tid; col < G * EQ; col += kRankThreads) {
+            const int eq = col % EQ;
+            const int g = col / EQ;
+            i32x4 total = {0, 0, 0, 0}, before = {0, 0, 0, 0};
+            for (int t0 = g; t0 < B; t0 += G * kHistBatch) {
+                i32x4 h[kHistBatch];
 #pragma unroll
-            for (int q = 0; q < kHistBatch; ++q) {
-                const int t = t0 + q * G;
-                h[q] = t < B ? tile_hist[(int64_t)t * E + e] : 0;
+                for (int q = 0; q < kHistBatch; ++q) {
+                    const int t = t0 + q * G;
+                    h[q] = hist4[(int64_t)(t < B ? t : B - 1) * EQ + eq];
+                }
+#pragma unroll
+                for (int q = 0; q < kHistBatch; ++q) {
+                    const int t = t0 + q * G;
+                    const i32x4 v = t < B ? h[q] : i32x4{0, 0, 0, 0};
+                    total += v;
+                    before += t < b ? v : i32x4{0, 0, 0, 0};
+                }
             }
 #pragma unroll
-            for (int q = 0; q < kHistBatch; ++q) {
-                total += h[q];
-                before += t0 + q * G < b ? h[q] : 0;
+            for (int c = 0; c < 4; ++c) {
+                atomicAdd(&cnt[4 * eq + c], total[c]);
+                atomicAdd(&base[4 * eq + c], before[c]);
             }
         }
-        atomicAdd(&cnt[e], total);
-        atomicAdd(&base[e], before);
+    } else {
+        const int G = max(1, min(E <= kRankThreads ? kRankThreads / E : 1, per_batch));
+        for (int col = tid; col < G * E; col += kRankThreads) {
+            const int e = col % E;
+            const int g = col / E;
+            int32_t total = 0, before = 0;
+            for (int t0 = g; t0 < B; t0 += G * kHistBatch) {
+                int32_t h[kHistBatch];
+#pragma unroll
+                for (int q = 0; q < kHistBatch; ++q) {
+                    const int t = t0 + q * G;
+                    h[q] = tile_hist[(int64_t)(t < B ? t : B - 1) * E + e];
+                }
+#pragma unroll
+                for (int q = 0; q < kHistBatch; ++q) {
+                    const int t = t0 + q * G;
+                    total += t < B ? h[q] : 0;
+                    before += t < b ? h[q] : 0;
+                }
+            }
+            atomicAdd(&cnt[e], total);
+            atomicAdd(&base[e], before);
+        }
     }
     __syncthreads();
     for (int e = tid; e < E; e += kRankThreads) {
