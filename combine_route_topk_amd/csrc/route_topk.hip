@@ -298,8 +298,9 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
 #pragma unroll
             for (int i = 0; i < NSLOT; ++i) {
                 const uint32_t id = slot_id<VEC, HW>(i, gl);
-                const uint32_t kk =
-                    (key[i] < gone_k || (key[i] == gone_k && id > gone_i)) ? key[i] : 0u;
+                // bitwise, not short-circuit: a select per slot, no branches
+                const bool below = (key[i] < gone_k) | ((key[i] == gone_k) & (id > gone_i));
+                const uint32_t kk = below ? key[i] : 0u;
                 const bool gt1 = kk > c1k, gt2 = kk > c2k;
                 c2k = gt1 ? c1k : (gt2 ? kk : c2k);
                 c2i = gt1 ? c1i : (gt2 ? id : c2i);
