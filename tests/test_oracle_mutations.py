@@ -14,7 +14,8 @@ import pytest
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 SRC = os.path.join(ROOT, "oracle", "oracle.c")
 PIN_TESTS = ["tests/test_oracle_route.py", "tests/test_oracle_layout.py", "tests/test_oracle_combine.py",
-             "tests/test_oracle_regroup.py", "tests/test_oracle_fp8.py", "tests/test_oracle_expert.py"]
+             "tests/test_oracle_regroup.py", "tests/test_oracle_fp8.py", "tests/test_oracle_expert.py",
+             "tests/test_oracle_properties.py"]
 
 MUTATIONS = {
     "tie_break_to_higher_id": ("    return ia < ib;\n", "    return ia > ib;\n"),
