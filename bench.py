@@ -341,6 +341,20 @@ def bench_tile_return(moe, torch, lay, send, S, El, H, rows, stream, warmup, ste
     return out
 
 
+def host_cpu():
+    """CPU model name (from /proc/cpuinfo) and the cores this process may run on."""
+    model = platform.processor() or platform.machine()
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, len(os.sched_getaffinity(0))
+
+
 def cpu_baseline(w, d, budget_s):
     """Time the single-threaded C oracle over the same workload."""
     import oracle
@@ -644,11 +658,13 @@ def main():
     if not args.no_cpu_baseline:
         log("cpu baseline: timing the C oracle on the same host arrays")
         sec, reps = cpu_baseline(w, d, args.cpu_seconds)
+        model, affinity = host_cpu()
         result["cpu_baseline"] = {
             "value": round(total / sec / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"the full {w.name} batch (T={T}), {reps} rep(s), median {sec:.2f}s per pass; "
-                      f"single-threaded C oracle on {platform.processor() or platform.machine()}",
+                      f"single-threaded C oracle on {model}",
             "tokens_per_s": round(T / sec, 1),
+            "host": {"cpu_model": model, "affinity_cores": affinity, "threads_used": 1},
         }
         log("cpu baseline", result["cpu_baseline"])
     print(json.dumps(result), flush=True)

@@ -21,13 +21,18 @@
 // Either way a lane's slots are in ascending expert order. For small rows
 // (E <= 128) each 32-lane half of the wave routes its own token, with the
 // same steps over half-wave reductions. Scores become
-// order-preserving 32-bit keys and each lane keeps its two best remaining
-// (key, id) candidates, built without branches. A selection round is a
-// wave-wide 32-bit maximum by DPP (six fused max steps, one readlane), a
-// ballot of the lanes holding that key and -- only when two lanes hold an
+// order-preserving 32-bit keys and each lane keeps its two or three best
+// remaining (key, id) candidates, built without branches. A selection round
+// is a wave-wide 32-bit maximum by DPP (six fused max steps, one readlane),
+// a ballot of the lanes holding that key and -- only when two lanes hold an
 // equal key -- a DPP minimum of their ids, so ties go to the smaller id.
 // The winning lane pops its candidate; it rescans its registers only once
-// both candidates are used (rare: a lane must win three of the k rounds).
+// every candidate is used. With 16-byte loads a lane holds runs of four
+// consecutive experts, so a skewed router that favours low ids makes one
+// lane win often: at E = 512, k = 10 with a Zipf-like skew a token needed
+// 1.5 rescans on average with two candidates and 0.3 with three, which is
+// why lanes with 8 or more slots (E > 256 with 16-byte loads) keep three
+// when k >= 3.
 // Lane j keeps round j's id; at the end lanes 0..k-1 gather their unbiased
 // logits from the row (still in cache), take the softmax and write one
 // coalesced row of ids and weights.
@@ -51,6 +56,27 @@ __device__ __forceinline__ uint32_t score_key(float s)
     const uint32_t u = __float_as_uint(s);
     const uint32_t k = u ^ (uint32_t)(((int32_t)u >> 31) | (int32_t)0x80000000);
     return s != s ? 1u : k;
+}
+
+// Insert (kk, id) into a lane's NC (2 or 3) best (key, id) candidates,
+// kept in rank order; with NC = 2 the third stays empty (key 0). Callers
+// present ids in ascending order, so the strict comparisons keep the
+// smaller id ahead of an equal key; key 0 (padding or already taken) never
+// enters.
+template <int NC>
+__device__ __forceinline__ void insert_cand(uint32_t kk, uint32_t id, uint32_t &c1k, uint32_t &c1i,
+                                            uint32_t &c2k, uint32_t &c2i, uint32_t &c3k, uint32_t &c3i)
+{
+    const bool gt1 = kk > c1k, gt2 = kk > c2k;
+    if (NC == 3) {
+        const bool gt3 = kk > c3k;
+        c3k = gt2 ? c2k : (gt3 ? kk : c3k);
+        c3i = gt2 ? c2i : (gt3 ? id : c3i);
+    }
+    c2k = gt1 ? c1k : (gt2 ? kk : c2k);
+    c2i = gt1 ? c1i : (gt2 ? id : c2i);
+    c1k = gt1 ? kk : c1k;
+    c1i = gt1 ? id : c1i;
 }
 
 // TPW tokens per wave: token h of the wave lives on lanes [h*HW, (h+1)*HW),
@@ -113,8 +139,8 @@ __device__ __forceinline__ int owner_lane(uint32_t e)
 
 // NSLOT keys per lane; VEC = 4 (16-byte loads) or 1 (4-byte loads); TPW
 // tokens per wave (2: each 32-lane half routes its own token, halving the
-// cost of the selection rounds per token)
-template <int NSLOT, int VEC, bool NORMALIZE, int TPW>
+// cost of the selection rounds per token); NC candidates per lane (2 or 3)
+template <int NSLOT, int VEC, bool NORMALIZE, int TPW, int NC>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int64_t T, int32_t E,
     int32_t k, int32_t n_groups, int32_t topk_groups, int32_t *__restrict__ topk_idx,
@@ -246,18 +272,12 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
             key[i] = ((chosen >> gid[i]) & 1ull) ? key[i] : 0u;
     }
 
-    // the lane's two best entries; ascending i is ascending id, so strict
-    // comparisons keep the smaller id first among equal keys
-    uint32_t c1k = key[0], c1i = slot_id<VEC, HW>(0, gl), c2k = 0u, c2i = 0xFFFFFFFFu;
+    // the lane's NC best entries
+    uint32_t c1k = key[0], c1i = slot_id<VEC, HW>(0, gl);
+    uint32_t c2k = 0u, c2i = 0xFFFFFFFFu, c3k = 0u, c3i = 0xFFFFFFFFu;
 #pragma unroll
-    for (int i = 1; i < NSLOT; ++i) {
-        const uint32_t kk = key[i], id = slot_id<VEC, HW>(i, gl);
-        const bool gt1 = kk > c1k, gt2 = kk > c2k;
-        c2k = gt1 ? c1k : (gt2 ? kk : c2k);
-        c2i = gt1 ? c1i : (gt2 ? id : c2i);
-        c1k = gt1 ? kk : c1k;
-        c1i = gt1 ? id : c1i;
-    }
+    for (int i = 1; i < NSLOT; ++i)
+        insert_cand<NC>(key[i], slot_id<VEC, HW>(i, gl), c1k, c1i, c2k, c2i, c3k, c3i);
 
     uint32_t my_e = 0;
     for (int j = 0; j < k; ++j) {
@@ -290,22 +310,23 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
         const uint32_t gone_k = c1k, gone_i = c1i;
         c1k = own ? c2k : c1k;
         c1i = own ? c2i : c1i;
-        c2k = own ? 0u : c2k;
+        if (NC == 3) {
+            c2k = own ? c3k : c2k;
+            c2i = own ? c3i : c2i;
+            c3k = own ? 0u : c3k;
+        } else {
+            c2k = own ? 0u : c2k;  // an empty slot's id is never read
+        }
         if (own && c1k == 0u) {
-            // both candidates used: rescan the entries ranked below the last
+            // every candidate used: rescan the entries ranked below the last
             // one taken from this lane
-            c2i = 0xFFFFFFFFu;
+            c1i = c2i = c3i = 0xFFFFFFFFu;
 #pragma unroll
             for (int i = 0; i < NSLOT; ++i) {
                 const uint32_t id = slot_id<VEC, HW>(i, gl);
                 // bitwise, not short-circuit: a select per slot, no branches
                 const bool below = (key[i] < gone_k) | ((key[i] == gone_k) & (id > gone_i));
-                const uint32_t kk = below ? key[i] : 0u;
-                const bool gt1 = kk > c1k, gt2 = kk > c2k;
-                c2k = gt1 ? c1k : (gt2 ? kk : c2k);
-                c2i = gt1 ? c1i : (gt2 ? id : c2i);
-                c1k = gt1 ? kk : c1k;
-                c1i = gt1 ? id : c1i;
+                insert_cand<NC>(below ? key[i] : 0u, id, c1k, c1i, c2k, c2i, c3k, c3i);
             }
         }
     }
@@ -336,19 +357,40 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     }
 }
 
+template <int NSLOT, int VEC, int TPW, int NC>
+void launch_cand(const float *logits, const float *bias, int64_t T, int32_t E, int32_t k,
+                 int32_t n_groups, int32_t topk_groups, bool normalize, int32_t *topk_idx,
+                 float *topk_w, hipStream_t stream)
+{
+    const int64_t per_block = (int64_t)kWavesPerBlock * TPW;
+    const dim3 grid((unsigned)((T + per_block - 1) / per_block));
+    if (normalize)
+        hipLaunchKernelGGL((route_topk_kernel<NSLOT, VEC, true, TPW, NC>), grid, dim3(kRouteThreads),
+                           0, stream, logits, bias, T, E, k, n_groups, topk_groups, topk_idx, topk_w);
+    else
+        hipLaunchKernelGGL((route_topk_kernel<NSLOT, VEC, false, TPW, NC>), grid, dim3(kRouteThreads),
+                           0, stream, logits, bias, T, E, k, n_groups, topk_groups, topk_idx, topk_w);
+}
+
 template <int NSLOT, int VEC, int TPW>
 hipError_t launch_slots(const float *logits, const float *bias, int64_t T, int32_t E, int32_t k,
                         int32_t n_groups, int32_t topk_groups, bool normalize, int32_t *topk_idx,
                         float *topk_w, hipStream_t stream)
 {
-    const int64_t per_block = (int64_t)kWavesPerBlock * TPW;
-    const dim3 grid((unsigned)((T + per_block - 1) / per_block));
-    if (normalize)
-        hipLaunchKernelGGL((route_topk_kernel<NSLOT, VEC, true, TPW>), grid, dim3(kRouteThreads), 0,
-                           stream, logits, bias, T, E, k, n_groups, topk_groups, topk_idx, topk_w);
-    else
-        hipLaunchKernelGGL((route_topk_kernel<NSLOT, VEC, false, TPW>), grid, dim3(kRouteThreads), 0,
-                           stream, logits, bias, T, E, k, n_groups, topk_groups, topk_idx, topk_w);
+    // A third candidate costs every token a few instructions per slot and
+    // saves the lanes that win three times a rescan of all their slots. On
+    // MI355X it paid with 8 or more slots per lane and k >= 3 (E = 512,
+    // k = 10: 28.2 against 30.8 us for 32768 tokens) and lost with 4 slots
+    // (E = 256, k = 8: 18.5 against 18.0 us).
+    if constexpr (NSLOT >= 8) {
+        if (k >= 3) {
+            launch_cand<NSLOT, VEC, TPW, 3>(logits, bias, T, E, k, n_groups, topk_groups, normalize,
+                                            topk_idx, topk_w, stream);
+            return hipGetLastError();
+        }
+    }
+    launch_cand<NSLOT, VEC, TPW, 2>(logits, bias, T, E, k, n_groups, topk_groups, normalize,
+                                    topk_idx, topk_w, stream);
     return hipGetLastError();
 }
 

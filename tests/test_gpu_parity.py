@@ -255,6 +255,8 @@ SHAPES = [
     (16, 65536, 16, 2, 4, -1),    # largest H: 16 slabs of 4096 values per row
     (262144, 8, 64, 8, 8, -1),    # 2^21 assignments: 128 tiles of 16384 (the tile grows past the cap)
     (32768, 8, 1024, 32, 64, -1),  # 2^20 assignments at the largest E and k (8 waves per rank block)
+    (3000, 8, 512, 2, 8, -1),     # 8 slots per lane with k <= 2: two route candidates
+    (601, 8, 902, 5, 11, -1),     # 4-byte route loads with 15 slots per lane, three candidates
 ]
 
 
@@ -385,6 +387,47 @@ def test_reproducible(moe):
         outs.append([t.cpu() for t in (idx, wt, L["pos"], L["send_src"][:N], send[:N], out)])
     for a, b in zip(*outs):
         assert np.array_equal(a.contiguous().view(torch.uint8).numpy(), b.contiguous().view(torch.uint8).numpy())
+
+
+def _lane_experts(E, lane):
+    """Experts whose logits one lane of the route kernel holds: runs of four
+    (4l..4l+3, then +256) with 16-byte loads (E % 4 == 0), else l + 64i."""
+    if E % 4 == 0:
+        ids = [256 * q + 4 * lane + c for q in range((E + 255) // 256) for c in range(4)]
+    else:
+        ids = [lane + 64 * i for i in range((E + 63) // 64)]
+    return np.array([e for e in ids if e < E])
+
+
+@pytest.mark.parametrize("E,k", [(512, 10), (512, 3), (512, 2), (1024, 32), (1024, 1), (300, 16),
+                                 (902, 5), (902, 2)])
+def test_route_candidate_rescans(moe, E, k):
+    """Rows that make one lane win round after round (so it must refill its
+    candidates from its registers, possibly several times), rows of ties and
+    special values, and all-equal rows, on row widths whose lanes hold 8 or
+    more slots."""
+    T = 1024
+    r = np.random.default_rng(E * 100 + k)
+    pool = np.array([0.0, -0.0, 1.0, -1.0, 0.5, 2.0, np.inf, -np.inf, np.nan], np.float32)
+    logits = r.choice(pool, size=(T, E)).astype(np.float32)        # rows 0, 4, ...: ties everywhere
+    logits[1::4] = r.standard_normal((len(range(1, T, 4)), E), dtype=np.float32)
+    top = r.standard_normal((len(range(2, T, 4)), E), dtype=np.float32) - 10.0
+    for n, row in enumerate(range(2, T, 4)):
+        ids = _lane_experts(E, n % 64)                               # one lane holds the best
+        top[n, ids] = 10.0 + r.standard_normal(len(ids), dtype=np.float32)
+        if n % 2:
+            top[n, ids[::2]] = 10.0                                  # with exact ties inside it
+    logits[2::4] = top
+    logits[3::4] = 0.0                                               # all equal: ids 0..k-1
+    say(f"route candidate rescans T={T} E={E} k={k}")
+    idx, wt = moe.moe_route_topk(up(logits), None, k)
+    torch.cuda.synchronize()
+    o_idx, o_w = oracle.route_topk(logits, None, k)
+    np.testing.assert_array_equal(idx.cpu().numpy(), o_idx)
+    assert np.all(o_idx[3::4] == np.arange(k))
+    fin = np.all(np.isfinite(np.take_along_axis(logits, o_idx.astype(np.int64), axis=1)), axis=1)
+    tol = weight_tolerance(logits[fin], o_idx[fin], o_w[fin], k)
+    assert np.all(np.abs(wt.cpu().numpy()[fin] - o_w[fin]) <= tol)
 
 
 @pytest.mark.parametrize("E", [512, 384])
