@@ -64,6 +64,17 @@ __device__ __forceinline__ uint32_t readlane_u32(uint32_t v, int lane)
     return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
 }
 
+// The compiler's writelane intrinsic, which this clang exposes under no
+// builtin name: bound to the intrinsic itself, so instruction selection and
+// hazard handling treat it like any other.
+__device__ int amdgcn_writelane_i32(int x, int lane, int v) __asm("llvm.amdgcn.writelane.i32");
+
+// v with lane `lane` replaced by the wave-uniform value x (one v_writelane)
+__device__ __forceinline__ uint32_t writelane_u32(uint32_t x, int lane, uint32_t v)
+{
+    return (uint32_t)amdgcn_writelane_i32((int)x, lane, (int)v);
+}
+
 // bf16 <-> float. A bf16 value is the top half of a float32 pattern, so
 // widening is a shift; narrowing uses gfx950's packed convert, which rounds
 // to nearest, ties to even, and quiets NaNs.

@@ -305,9 +305,13 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
             ew = G::min_u32(c1k == best ? c1i : 0xFFFFFFFFu);
             owner = gbase + owner_lane<VEC, HW>(ew);
         }
-        my_e = gl == j ? ew : my_e;
+        // lane j keeps round j's id: one writelane of the uniform id with one
+        // token per wave, a select per half with two
+        my_e = TPW == 1 ? writelane_u32(ew, j, my_e) : (gl == j ? ew : my_e);
         const bool own = lane == owner;
-        const uint32_t gone_k = c1k, gone_i = c1i;
+        // in the owner lane the candidate taken is (best, ew): the round's
+        // uniform key and id, so the pop below can overwrite c1 in place
+        const uint32_t gone_k = best, gone_i = ew;
         c1k = own ? c2k : c1k;
         c1i = own ? c2i : c1i;
         if (NC == 3) {
