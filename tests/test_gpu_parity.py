@@ -396,24 +396,26 @@ def _lane_experts(E, lane):
         ids = [256 * q + 4 * lane + c for q in range((E + 255) // 256) for c in range(4)]
     else:
         ids = [lane + 64 * i for i in range((E + 63) // 64)]
-    return np.array([e for e in ids if e < E])
+    return np.array([e for e in ids if e < E], dtype=np.int64)
 
 
 @pytest.mark.parametrize("E,k", [(512, 10), (512, 3), (512, 2), (1024, 32), (1024, 1), (300, 16),
-                                 (902, 5), (902, 2)])
+                                 (902, 5), (902, 2), (64, 8), (128, 16), (100, 7), (30, 6)])
 def test_route_candidate_rescans(moe, E, k):
     """Rows that make one lane win round after round (so it must refill its
     candidates from its registers, possibly several times), rows of ties and
-    special values, and all-equal rows, on row widths whose lanes hold 8 or
-    more slots."""
+    special values, and all-equal rows: on row widths whose lanes hold 8 or
+    more slots (three candidates when k >= 3), and on rows of at most 128
+    experts, where each 32-lane half of a wave routes its own token."""
     T = 1024
     r = np.random.default_rng(E * 100 + k)
     pool = np.array([0.0, -0.0, 1.0, -1.0, 0.5, 2.0, np.inf, -np.inf, np.nan], np.float32)
     logits = r.choice(pool, size=(T, E)).astype(np.float32)        # rows 0, 4, ...: ties everywhere
     logits[1::4] = r.standard_normal((len(range(1, T, 4)), E), dtype=np.float32)
     top = r.standard_normal((len(range(2, T, 4)), E), dtype=np.float32) - 10.0
+    two = (E <= 128) if E % 4 == 0 else (E <= 32)                    # 32 lanes per token
     for n, row in enumerate(range(2, T, 4)):
-        ids = _lane_experts(E, n % 64)                               # one lane holds the best
+        ids = _lane_experts(E, n % (32 if two else 64))              # one lane holds the best
         top[n, ids] = 10.0 + r.standard_normal(len(ids), dtype=np.float32)
         if n % 2:
             top[n, ids[::2]] = 10.0                                  # with exact ties inside it
