@@ -139,8 +139,10 @@ __device__ __forceinline__ int owner_lane(uint32_t e)
 
 // NSLOT keys per lane; VEC = 4 (16-byte loads) or 1 (4-byte loads); TPW
 // tokens per wave (2: each 32-lane half routes its own token, halving the
-// cost of the selection rounds per token); NC candidates per lane (2 or 3)
-template <int NSLOT, int VEC, bool NORMALIZE, int TPW, int NC>
+// cost of the selection rounds per token); NC candidates per lane (2 or 3);
+// BIAS: a selection bias is given (without it, each slot's score costs two
+// fewer instructions than a select between the biased and unbiased value)
+template <int NSLOT, int VEC, bool NORMALIZE, int TPW, int NC, bool BIAS>
 __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     const float *__restrict__ logits, const float *__restrict__ bias, int64_t T, int32_t E,
     int32_t k, int32_t n_groups, int32_t topk_groups, int32_t *__restrict__ topk_idx,
@@ -166,10 +168,10 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
         for (int g = 0; g < NSLOT / 4; ++g) {
             if (valid && g * 4 * HW + 4 * gl < E) {
                 const f32x4 v = __builtin_nontemporal_load(row4 + g * HW + gl);
-                const f32x4 b = bias ? bias4[g * HW + gl] : f32x4{0.f, 0.f, 0.f, 0.f};
+                const f32x4 b = BIAS ? bias4[g * HW + gl] : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
-                    key[4 * g + c] = score_key((bias ? v[c] + b[c] : v[c]) + 0.0f);
+                    key[4 * g + c] = score_key((BIAS ? v[c] + b[c] : v[c]) + 0.0f);
             } else {
 #pragma unroll
                 for (int c = 0; c < 4; ++c)
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
             const int e = i * HW + gl;
             if (valid && e < E) {
                 const float v = row[e];
-                key[i] = score_key((bias ? v + bias[e] : v) + 0.0f);
+                key[i] = score_key((BIAS ? v + bias[e] : v) + 0.0f);
             } else {
                 key[i] = 0u;  // padding ranks below everything, NaN included
             }
@@ -368,12 +370,21 @@ void launch_cand(const float *logits, const float *bias, int64_t T, int32_t E, i
 {
     const int64_t per_block = (int64_t)kWavesPerBlock * TPW;
     const dim3 grid((unsigned)((T + per_block - 1) / per_block));
-    if (normalize)
-        hipLaunchKernelGGL((route_topk_kernel<NSLOT, VEC, true, TPW, NC>), grid, dim3(kRouteThreads),
-                           0, stream, logits, bias, T, E, k, n_groups, topk_groups, topk_idx, topk_w);
-    else
-        hipLaunchKernelGGL((route_topk_kernel<NSLOT, VEC, false, TPW, NC>), grid, dim3(kRouteThreads),
-                           0, stream, logits, bias, T, E, k, n_groups, topk_groups, topk_idx, topk_w);
+#define MOE_ROUTE_LAUNCH(N, B)                                                                      \
+    hipLaunchKernelGGL((route_topk_kernel<NSLOT, VEC, N, TPW, NC, B>), grid, dim3(kRouteThreads), 0, \
+                       stream, logits, bias, T, E, k, n_groups, topk_groups, topk_idx, topk_w)
+    if (normalize) {
+        if (bias)
+            MOE_ROUTE_LAUNCH(true, true);
+        else
+            MOE_ROUTE_LAUNCH(true, false);
+    } else {
+        if (bias)
+            MOE_ROUTE_LAUNCH(false, true);
+        else
+            MOE_ROUTE_LAUNCH(false, false);
+    }
+#undef MOE_ROUTE_LAUNCH
 }
 
 template <int NSLOT, int VEC, int TPW>
