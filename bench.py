@@ -341,6 +341,16 @@ def bench_tile_return(moe, torch, lay, send, S, El, H, rows, stream, warmup, ste
     return out
 
 
+def load_balance(demand, kept, dest_rows):
+    """Load imbalance from the layout's own counts: max / mean per expert
+    (demand and kept rows) and per destination, since a skewed router makes
+    the busiest expert and the busiest destination set the time."""
+    ratio = lambda a: round(float(a.max() / a.mean()), 3) if a.size and a.mean() > 0 else None
+    return {"expert_demand_max_over_mean": ratio(demand), "expert_kept_max_over_mean": ratio(kept),
+            "dest_rows_max_over_mean": ratio(dest_rows), "hot_dest_rows": int(dest_rows.max()),
+            "dropped": int(demand.sum() - kept.sum())}
+
+
 def host_cpu():
     """CPU model name (from /proc/cpuinfo) and the cores this process may run on."""
     model = platform.processor() or platform.machine()
@@ -550,6 +560,9 @@ def main():
     # bookkeeping from the path's own outputs (outside the timed region)
     N = int(lay["expert_offsets"][E].item())
     T_read = int((lay["pos"] >= 0).any(dim=1).sum().item())
+    load = load_balance(lay["expert_demand"].cpu().numpy(), lay["expert_counts"].cpu().numpy(),
+                        lay["dest_counts"].cpu().numpy())
+    log("load", load)
     nbytes = algorithmic_bytes(w, N, T_read, bias is not None)
     total = sum(nbytes.values())
     gbps = total / (ms_per_step * 1e-3) / 1e9
@@ -653,6 +666,7 @@ def main():
         next_rows["tile_signalled_return"] = tile_return
     if next_rows:
         result["next_rows"] = next_rows
+    result["load"] = load
     if floor:
         result["synthetic_floor"] = floor
     if copy_probe:

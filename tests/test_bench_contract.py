@@ -83,3 +83,16 @@ def test_committed_traffic_records_match_sources(bench):
     stand; a stale one would make the benchmark report no traffic."""
     for kernel in bench.KERNEL_SOURCES:
         assert bench.stored_traffic(kernel, "fine_grained") is not None, kernel
+
+
+def test_load_balance_hand_case(bench):
+    import numpy as np
+    # 4 experts on 2 destinations: demand 6, 2, 0, 0 with capacity 3 keeps 3, 2, 0, 0
+    demand = np.array([6, 2, 0, 0], np.int32)
+    kept = np.array([3, 2, 0, 0], np.int32)
+    dest = np.array([5, 0], np.int32)
+    got = bench.load_balance(demand, kept, dest)
+    assert got == {"expert_demand_max_over_mean": 3.0, "expert_kept_max_over_mean": 2.4,
+                   "dest_rows_max_over_mean": 2.0, "hot_dest_rows": 5, "dropped": 3}
+    assert bench.load_balance(np.zeros(4, np.int32), np.zeros(4, np.int32), np.zeros(2, np.int32))[
+        "expert_demand_max_over_mean"] is None
