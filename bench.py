@@ -89,6 +89,8 @@ def parse():
                    help="skip the cold-cache pass (each step after a 1 GiB scratch read)")
     p.add_argument("--no-floor", action="store_true",
                    help="skip the synthetic floor (a device-to-device copy of the step's bytes)")
+    p.add_argument("--no-pipelined", action="store_true",
+                   help="skip the pass with two batches in flight on two streams (reported beside value)")
     p.add_argument("--no-fp8", action="store_true",
                    help="skip the FP8-payload step measurement (reported under next_rows)")
     p.add_argument("--no-tile-return", action="store_true",
@@ -419,15 +421,23 @@ def main():
     T, H, E, k, R, C = w.T, w.H, w.E, w.k, w.R, w.capacity
     send_rows = T * k if C < 0 else min(T * k, E * C)
     i32 = dict(dtype=torch.int32, device=dev)
-    idx = torch.empty((T, k), **i32)
-    wt = torch.empty((T, k), dtype=torch.float32, device=dev)
-    lay = {"expert_demand": torch.empty(E, **i32), "expert_counts": torch.empty(E, **i32),
-           "expert_offsets": torch.empty(E + 1, **i32), "dest_counts": torch.empty(R, **i32),
-           "dest_offsets": torch.empty(R + 1, **i32), "pos": torch.empty((T, k), **i32),
-           "send_src": torch.empty(T * k, **i32)}
-    ws = torch.empty(max(moe.moe_layout_workspace_size(T, E, k, R), 16), dtype=torch.uint8, device=dev)
-    send = torch.empty((send_rows, H), dtype=torch.bfloat16, device=dev)
-    out = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+
+    def output_set():
+        """Everything one step writes: routing, layout, workspace, send rows, output."""
+        return {"idx": torch.empty((T, k), **i32),
+                "wt": torch.empty((T, k), dtype=torch.float32, device=dev),
+                "lay": {"expert_demand": torch.empty(E, **i32), "expert_counts": torch.empty(E, **i32),
+                        "expert_offsets": torch.empty(E + 1, **i32), "dest_counts": torch.empty(R, **i32),
+                        "dest_offsets": torch.empty(R + 1, **i32), "pos": torch.empty((T, k), **i32),
+                        "send_src": torch.empty(T * k, **i32)},
+                "ws": torch.empty(max(moe.moe_layout_workspace_size(T, E, k, R), 16), dtype=torch.uint8,
+                                  device=dev),
+                "send": torch.empty((send_rows, H), dtype=torch.bfloat16, device=dev),
+                "out": torch.empty((T, H), dtype=torch.bfloat16, device=dev)}
+
+    main_set = output_set()
+    idx, wt, lay, ws = main_set["idx"], main_set["wt"], main_set["lay"], main_set["ws"]
+    send, out = main_set["send"], main_set["out"]
     stream = torch.cuda.current_stream()
     sp = stream.cuda_stream
     groups = None if args.route_groups is None else tuple(int(v) for v in args.route_groups.split(","))
@@ -438,7 +448,8 @@ def main():
         if rc != moe.MOE_OK:
             raise RuntimeError(f"{name}: {moe.moe_status_string(rc)}")
 
-    def make_calls(sp):
+    def make_calls(sp, o=main_set):
+        idx, wt, lay, ws, send, out = o["idx"], o["wt"], o["lay"], o["ws"], o["send"], o["out"]
         return [
             ("route", lambda: check("route", lib.moe_route_topk(
                 P(logits), P(bias), T, E, k, moe.MOE_ROUTE_NORMALIZE, P(idx), P(wt), sp))
@@ -557,6 +568,46 @@ def main():
         del scratch
         log("cold-cache single-step us", cold)
 
+    # pass 5: K more steps with two batches in flight. Step s runs on stream
+    # s % 2 with its own outputs, so the routing and layout of one batch
+    # (bound by instruction issue and latency) can run beside the other's
+    # permute and combine (bound by HBM). Reported beside `value`, which stays
+    # the time of one step on its own. (Making each permute wait for the
+    # previous combine, so that only routing and layout overlap, measured
+    # slower: the cross-stream waits cost more than they saved.)
+    ms_pipe, pipe_equal = None, None
+    if not args.no_pipelined:
+        ref_out = out.clone()                     # a step on its own, from the passes above
+        sets = [main_set, output_set()]
+        pstreams = [torch.cuda.Stream(), torch.cuda.Stream()]  # default priority
+        pcalls = [make_calls(ps.cuda_stream, o) for ps, o in zip(pstreams, sets)]
+
+        def run_pipelined(n):
+            fork = torch.cuda.Event()
+            fork.record(stream)
+            for ps in pstreams:
+                ps.wait_event(fork)
+            for s in range(n):
+                for _, fn in pcalls[s % 2]:
+                    fn()
+            for ps in pstreams:
+                joined = torch.cuda.Event()
+                joined.record(ps)
+                stream.wait_event(joined)
+
+        torch.cuda.synchronize()
+        run_pipelined(max(args.warmup, 2))
+        torch.cuda.synchronize()
+        pb, pe = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        pb.record(stream)
+        run_pipelined(args.steps)
+        pe.record(stream)
+        torch.cuda.synchronize()
+        ms_pipe = pb.elapsed_time(pe) / args.steps
+        pipe_equal = all(torch.equal(o["out"], ref_out) for o in sets)
+        del sets, pcalls, ref_out
+        log(f"two batches in flight: {ms_pipe * 1e3:.1f} us/step, outputs bitwise equal: {pipe_equal}")
+
     # bookkeeping from the path's own outputs (outside the timed region)
     N = int(lay["expert_offsets"][E].item())
     T_read = int((lay["pos"] >= 0).any(dim=1).sum().item())
@@ -667,6 +718,13 @@ def main():
     if next_rows:
         result["next_rows"] = next_rows
     result["load"] = load
+    if ms_pipe is not None:
+        result["pipelined_two_streams"] = {
+            "us_per_step": round(ms_pipe * 1e3, 1), "GBps": round(total / (ms_pipe * 1e-3) / 1e9, 1),
+            "tokens_per_s": round(T / (ms_pipe * 1e-3), 1),
+            "speedup_vs_one_step_at_a_time": round(ms_per_step / ms_pipe, 3),
+            "outputs_bitwise_equal": pipe_equal,
+            "note": "two batches in flight on two streams with their own outputs; `value` is one step at a time"}
     if floor:
         result["synthetic_floor"] = floor
     if copy_probe:
