@@ -486,3 +486,34 @@ def test_route_topk_grouped(moe, case):
     finite = np.isfinite(o_w).all(axis=1)
     tol = weight_tolerance(logits, o_idx, o_w, k)
     assert np.all(np.abs(wt.cpu().numpy() - o_w)[finite] <= tol[finite])
+
+
+@pytest.mark.parametrize("E,k,G,M", [(512, 10, 8, 4), (1024, 12, 16, 3), (384, 8, 64, 4), (120, 6, 8, 3)])
+def test_route_grouped_ties_and_specials(moe, E, k, G, M):
+    """Group-limited routing on rows full of ties, signed zeros, infinities
+    and NaNs (group maxima tie too), on rows where one lane holds the best
+    experts of its groups, and on all-equal rows (the lowest groups and ids
+    win)."""
+    T = 1024
+    r = np.random.default_rng(E + k + G)
+    pool = np.array([0.0, -0.0, 1.0, -1.0, 2.0, np.inf, -np.inf, np.nan], np.float32)
+    logits = r.choice(pool, size=(T, E)).astype(np.float32)
+    logits[1::3] = r.standard_normal((len(range(1, T, 3)), E), dtype=np.float32) - 10.0
+    two = (E <= 128) if E % 4 == 0 else (E <= 32)
+    for n, row in enumerate(range(1, T, 3)):
+        ids = _lane_experts(E, n % (32 if two else 64))
+        logits[row, ids] = 10.0 + np.round(r.standard_normal(len(ids)), 1).astype(np.float32)
+    logits[2::3] = 0.0
+    bias = np.where(r.random(E) < 0.5, 0.0, 1.0).astype(np.float32)   # ties survive the bias
+    say(f"route grouped ties T={T} E={E} k={k} groups={G} topk_groups={M}")
+    for b in (None, bias):
+        idx, wt = moe.moe_route_topk_grouped(up(logits), None if b is None else up(b), k, G, M)
+        torch.cuda.synchronize()
+        o_idx, o_w = oracle.route_topk_grouped(logits, b, k, G, M)
+        np.testing.assert_array_equal(idx.cpu().numpy(), o_idx)
+        fin = np.all(np.isfinite(np.take_along_axis(logits, o_idx.astype(np.int64), axis=1)), axis=1)
+        tol = weight_tolerance(logits[fin], o_idx[fin], o_w[fin], k)
+        assert np.all(np.abs(wt.cpu().numpy()[fin] - o_w[fin]) <= tol)
+        if b is None:
+            # all-equal rows: groups 0..M-1 tie and win, and inside them the lowest ids
+            assert np.all(o_idx[2::3] == np.arange(k))
