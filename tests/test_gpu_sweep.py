@@ -23,7 +23,7 @@ DEV = "cuda:0"
 ATOL = 1e-5
 
 
-def make_cases(n=16, seed=2024):
+def make_cases(n=64, seed=2024):
     r = np.random.default_rng(seed)
     cases = []
     while len(cases) < n:
