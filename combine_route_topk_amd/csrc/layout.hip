@@ -376,7 +376,7 @@ LayoutPlan layout_plan(int64_t TK, int32_t E)
         p.tiles = 0;
         return p;
     }
-    int64_t tile = kLayoutTile;
+    int64_t tile = layout_min_tile(E);
     if ((TK + tile - 1) / tile > kMaxTiles) {
         const int64_t per = (TK + kMaxTiles - 1) / kMaxTiles;
         tile = (per + kLayoutThreads - 1) / kLayoutThreads * kLayoutThreads;

@@ -78,11 +78,13 @@ def test_grouped_route_validation(moe):
 
 
 def test_workspace_size(moe):
-    # one E-wide int32 histogram per tile: tiles of 2048 assignments, at most
-    # 128 of them; up to 4096 assignments (E <= 512) need no workspace
+    # one E-wide int32 histogram per tile: tiles of at least 512 assignments
+    # (E <= 128) or 1024 (larger E), at most 128 of them; up to 4096
+    # assignments (E <= 512) need no workspace
     assert moe.moe_layout_workspace_size(32768, 512, 10, 64) == 128 * 512 * 4
-    assert moe.moe_layout_workspace_size(8192, 64, 8, 8) == 32 * 64 * 4
-    assert moe.moe_layout_workspace_size(4096, 384, 8, 64) == 16 * 384 * 4
+    assert moe.moe_layout_workspace_size(8192, 64, 8, 8) == 128 * 64 * 4
+    assert moe.moe_layout_workspace_size(4096, 384, 8, 64) == 32 * 384 * 4
+    assert moe.moe_layout_workspace_size(4096, 128, 2, 8) == 16 * 128 * 4
     assert moe.moe_layout_workspace_size(512, 384, 8, 64) == 0
     assert moe.moe_layout_workspace_size(256, 16, 2, 4) == 0
     assert moe.moe_layout_workspace_size(256, 1024, 2, 4) == 1 * 1024 * 4
@@ -108,11 +110,11 @@ def test_layout_validation(moe):
     assert _layout(lib, idx=None) == moe.MOE_ERR_INVALID_ARG
     assert _layout(lib, pos=MIS) == moe.MOE_ERR_INVALID_ARG
     assert _layout(lib, out=None) == moe.MOE_ERR_INVALID_ARG
-    # 65536 assignments take the tiled layout: 32 tiles x 64 experts x 4 bytes
+    # 65536 assignments take the tiled layout: 128 tiles x 64 experts x 4 bytes
     big = dict(T=8192, E=64, k=8, R=8)
-    assert moe.moe_layout_workspace_size(8192, 64, 8, 8) == 8192
+    assert moe.moe_layout_workspace_size(8192, 64, 8, 8) == 32768
     assert _layout(lib, ws=None, **big) == moe.MOE_ERR_WORKSPACE
-    assert _layout(lib, ws_bytes=8191, **big) == moe.MOE_ERR_WORKSPACE
+    assert _layout(lib, ws_bytes=32767, **big) == moe.MOE_ERR_WORKSPACE
     assert _layout(lib, ws=FAKE + 8, **big) == moe.MOE_ERR_WORKSPACE
 
 
