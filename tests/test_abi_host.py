@@ -273,3 +273,29 @@ def test_binding_refuses_host_tensors(moe):
     with pytest.raises(ValueError):
         moe.moe_route_topk(torch.zeros(4, 8), None, 2, topk_idx=torch.zeros(4, 2, dtype=torch.int32),
                            topk_w=torch.zeros(4, 2), stream=0)
+
+
+def test_header_is_c_and_readme_example_compiles(tmp_path):
+    """include/moe_ep.h is plain C11, and the call sequence shown in the
+    README compiles against it (types and argument order)."""
+    import shutil
+    import subprocess
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("no gcc")
+    readme = open(os.path.join(root, "README.md")).read()
+    block = re.search(r"```c\n(.*?)```", readme, re.S).group(1)
+    src = tmp_path / "example.c"
+    src.write_text(
+        '#include "moe_ep.h"\n'
+        "void step(int64_t T, int32_t E, int32_t k, int32_t R, int32_t H, int32_t capacity, int64_t send_rows,\n"
+        "          const float *logits, const float *bias, const uint16_t *x, const uint16_t *shared,\n"
+        "          const uint16_t *residual, int32_t *topk_idx, float *topk_w, int32_t *expert_demand,\n"
+        "          int32_t *expert_counts, int32_t *expert_offsets, int32_t *dest_counts,\n"
+        "          int32_t *dest_offsets, int32_t *pos, int32_t *send_src, void *ws, uint16_t *send,\n"
+        "          const uint16_t *y, void *out, void *stream)\n{\n" + block + "(void)send;\n}\n")
+    r = subprocess.run([gcc, "-std=c11", "-Wall", "-Wextra", "-Werror", "-Wno-unused-parameter",
+                        "-I", os.path.join(root, "include"), "-c", str(src), "-o", str(tmp_path / "e.o")],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
