@@ -33,13 +33,17 @@ none part of `value`:
     tiles are returned as they finish, against the GEMM then a copy.
 
 Alongside: the spread of single-step times (a third pass with one event
-between steps), the same spread from a cold cache (a fourth pass, each step
-after a 1 GiB scratch read that evicts the Infinity Cache) and a synthetic
-floor -- a device-to-device copy moving the
-step's byte count, half read and half written, timed like the step -- as
-the achievable HBM rate for the same volume.
+between steps); the same spread from a cold cache (a fourth pass, each step
+after a 1 GiB scratch read that evicts the Infinity Cache); a fifth pass
+with two batches in flight on two streams, each with its own outputs, whose
+results must equal a step on its own bit for bit ("pipelined_two_streams");
+the load imbalance read from the layout's own counts ("load"); and a
+synthetic floor -- a device-to-device copy moving the step's byte count,
+half read and half written, timed like the step -- as the achievable HBM
+rate for the same volume.
 
-The CPU-baseline leg times the plain C oracle on the same host arrays.
+The CPU-baseline leg times the plain C oracle on the same host arrays:
+whole passes on one core for about --cpu-seconds, median pass.
 """
 
 from __future__ import annotations
