@@ -18,9 +18,12 @@
 // otherwise lane l owns experts l, l + 64, ... with 4-byte loads. On MI355X
 // the 16-byte form reads the logits at ~6.9 TB/s against ~2 TB/s for the
 // 4-byte form, which made the load phase the bottleneck of this kernel.
-// Either way a lane's slots are in ascending expert order. For small rows
-// (E <= 128) each 32-lane half of the wave routes its own token, with the
-// same steps over half-wave reductions. Scores become
+// Either way a lane's slots are in ascending expert order. Small rows share
+// a wave: with 16-byte loads and E <= 64 a token takes one DPP row or less
+// (4, 8 or 16 tokens per wave), its reductions are butterfly steps inside the
+// row, and a round's owner is the lane holding the smallest id among those
+// with the best key; for E <= 128 each 32-lane half routes its own token
+// with half-wave reductions. Scores become
 // order-preserving 32-bit keys and each lane keeps its two or three best
 // remaining (key, id) candidates, built without branches. A selection round
 // is a wave-wide 32-bit maximum by DPP (six fused max steps, one readlane),
@@ -90,8 +93,12 @@ struct Group {
     {
         v = op(v, dpp::mov<dpp::kQuadSwap1>(v, identity));
         v = op(v, dpp::mov<dpp::kQuadSwap2>(v, identity));
-        v = op(v, dpp::mov<dpp::kRowHalfMirror>(v, identity));
-        v = op(v, dpp::mov<dpp::kRowMirror>(v, identity));
+        if (HW >= 8)
+            v = op(v, dpp::mov<dpp::kRowHalfMirror>(v, identity));
+        if (HW >= 16)
+            v = op(v, dpp::mov<dpp::kRowMirror>(v, identity));
+        if (HW <= 16)
+            return v;  // butterfly steps inside a row: every lane holds its token's result
         v = op(v, dpp::mov<dpp::kRowBcast15, 0xA>(v, identity));
         if (TPW == 1) {
             v = op(v, dpp::mov<dpp::kRowBcast31, 0xC>(v, identity));
@@ -261,11 +268,18 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
             } else {
                 best = G::max_u32(my_gkey);
             }
-            const uint64_t holders = ballot64(my_gkey == best && gl < n_groups);
-            // the lowest holding lane of each token's lanes
-            const uint64_t mine = TPW == 1 ? holders
-                                           : (gbase == 0 ? holders & 0xFFFFFFFFull : holders >> 32);
-            const int g = __ffsll((unsigned long long)mine) - 1;
+            int g;
+            if (TPW >= 4) {
+                // the lowest group of the token holding the best key, by a
+                // minimum inside the token's row segment
+                g = (int)G::min_u32(((my_gkey == best) & (gl < n_groups)) ? (uint32_t)gl : 0xFFFFFFFFu);
+            } else {
+                const uint64_t holders = ballot64(my_gkey == best && gl < n_groups);
+                // the lowest holding lane of each token's lanes
+                const uint64_t mine = TPW == 1 ? holders
+                                               : (gbase == 0 ? holders & 0xFFFFFFFFull : holders >> 32);
+                g = __ffsll((unsigned long long)mine) - 1;
+            }
             chosen |= 1ull << g;
             my_gkey = gl == g ? 0u : my_gkey;
         }
@@ -284,33 +298,41 @@ __global__ __launch_bounds__(kRouteThreads) void route_topk_kernel(
     uint32_t my_e = 0;
     for (int j = 0; j < k; ++j) {
         const uint32_t best = G::max_u32(c1k);
-        const uint64_t holders = ballot64(c1k == best);
-        int owner;
         uint32_t ew;
-        bool unique;
-        if (TPW == 1)
-            unique = __popcll(holders) == 1;
-        else
-            unique = __popcll(holders & 0xFFFFFFFFull) == 1 && __popcll(holders >> 32) == 1;
-        if (unique) {
-            if (TPW == 1) {
-                owner = __ffsll((unsigned long long)holders) - 1;
-                ew = readlane_u32(c1i, owner);
-            } else {
-                const int o0 = __ffsll((unsigned long long)(holders & 0xFFFFFFFFull)) - 1;
-                const int o1 = 32 + __ffsll((unsigned long long)(holders >> 32)) - 1;
-                const uint32_t e0 = readlane_u32(c1i, o0), e1 = readlane_u32(c1i, o1);
-                owner = gbase == 0 ? o0 : o1;
-                ew = gbase == 0 ? e0 : e1;
-            }
-        } else {  // several lanes of a token hold an equal key: the smallest id wins
+        bool own;
+        if (TPW >= 4) {
+            // a token per row segment: the smallest id among the lanes holding
+            // the best key, by a minimum inside the segment; its lane owns it
             ew = G::min_u32(c1k == best ? c1i : 0xFFFFFFFFu);
-            owner = gbase + owner_lane<VEC, HW>(ew);
+            own = (c1k == best) & (c1i == ew);
+        } else {
+            const uint64_t holders = ballot64(c1k == best);
+            int owner;
+            bool unique;
+            if (TPW == 1)
+                unique = __popcll(holders) == 1;
+            else
+                unique = __popcll(holders & 0xFFFFFFFFull) == 1 && __popcll(holders >> 32) == 1;
+            if (unique) {
+                if (TPW == 1) {
+                    owner = __ffsll((unsigned long long)holders) - 1;
+                    ew = readlane_u32(c1i, owner);
+                } else {
+                    const int o0 = __ffsll((unsigned long long)(holders & 0xFFFFFFFFull)) - 1;
+                    const int o1 = 32 + __ffsll((unsigned long long)(holders >> 32)) - 1;
+                    const uint32_t e0 = readlane_u32(c1i, o0), e1 = readlane_u32(c1i, o1);
+                    owner = gbase == 0 ? o0 : o1;
+                    ew = gbase == 0 ? e0 : e1;
+                }
+            } else {  // several lanes of a token hold an equal key: the smallest id wins
+                ew = G::min_u32(c1k == best ? c1i : 0xFFFFFFFFu);
+                owner = gbase + owner_lane<VEC, HW>(ew);
+            }
+            own = lane == owner;
         }
         // lane j keeps round j's id: one writelane of the uniform id with one
-        // token per wave, a select per half with two
+        // token per wave, a select per token otherwise
         my_e = TPW == 1 ? writelane_u32(ew, j, my_e) : (gl == j ? ew : my_e);
-        const bool own = lane == owner;
         // in the owner lane the candidate taken is (best, ew): the round's
         // uniform key and id, so the pop below can overwrite c1 in place
         const uint32_t gone_k = best, gone_i = ew;
@@ -424,7 +446,21 @@ hipError_t launch_route_topk(const float *logits, const float *bias, int64_t T, 
     // E <= 128 with 16-byte loads, E <= 32 otherwise; and lane g of a half
     // must hold group g (<= 32 groups).
     const bool two = (vec4 ? E <= 4 * 32 : E <= 32) && n_groups <= 32;
+    // With 16-byte loads and E <= 64, a token fits one DPP row (16 lanes of 4
+    // experts) or less, so 4, 8 or 16 tokens share a wave: each reduction is
+    // 2-4 butterfly steps inside the row and needs no readlane. The row must
+    // also hold the k ids and one lane per group.
+    int seg = 4;
+    while (seg < (E + 3) / 4 || seg < k || seg < n_groups)
+        seg *= 2;
 #define MOE_ROUTE_ARGS logits, bias, T, E, k, n_groups, topk_groups, normalize, topk_idx, topk_w, stream
+    if (vec4 && seg <= 16) {
+        switch (seg) {
+        case 4: return launch_slots<4, 4, 16>(MOE_ROUTE_ARGS);
+        case 8: return launch_slots<4, 4, 8>(MOE_ROUTE_ARGS);
+        default: return launch_slots<4, 4, 4>(MOE_ROUTE_ARGS);
+        }
+    }
     if (vec4 && two) {
         return launch_slots<4, 4, 2>(MOE_ROUTE_ARGS);
     }
