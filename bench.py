@@ -7,8 +7,8 @@ buffer). W untimed warm-up steps, then exactly K timed steps between
 device synchronisations with HIP events only at the two ends (an event
 between calls leaves the GPU idle for a few microseconds). The steps are
 eager launches; --graph times replays of a HIP graph that holds the four
-launches instead (on MI355X a replay cost 40 us where the four eager
-launches of the decode workload cost 18 us, so eager is the default). A second pass of
+launches instead (on MI355X a replay cost 22 us where the four eager
+launches of the decode workload cost 16 us, so eager is the default). A second pass of
 K steps records an event pair around every call, on the stream the kernels
 run on, for the per-call durations and the roofline of the dominant kernel.
 
