@@ -100,10 +100,11 @@ def test_wide_dynamic_range(moe, H):
     check_rows(gpu_quantize(moe, x), x, H)
 
 
-@pytest.mark.parametrize("H", [32, 96, 160, 544, 4128])
+@pytest.mark.parametrize("H", [32, 96, 160, 544, 4128, 65536])
 def test_partial_wave_widths(moe, H):
     """Widths that leave lanes of the last wave (or slab) idle; the scale
-    line is zero after the row's last scale byte."""
+    line is zero after the row's last scale byte. H = 65536, the largest
+    width, gives 16 slabs and 16 scale lines per row."""
     r = np.random.default_rng(H)
     x = synthetic.bf16_bits_from_f32(r.standard_normal((37, H)).astype(np.float32) * 3)
     say(f"fp8 quantise partial-wave width H={H}")

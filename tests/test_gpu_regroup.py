@@ -109,6 +109,7 @@ SHAPES = [  # (S, E_l, max count, H)
     (4, 1024, 3, 16),       # E_l at its limit
     (64, 64, 2, 24),        # S*E_l at its limit, H not a multiple of 64
     (3, 5, 700, 4104),      # ragged slab tail: 4104 = 4096 + 8 columns
+    (2, 3, 5, 65536),       # the largest row width: 16 slabs per row
 ]
 
 
