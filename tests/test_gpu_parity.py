@@ -355,8 +355,11 @@ def test_invalid_ids_are_ignored(moe):
     assert np.array_equal(np.sort(pos[ok]), np.arange(ok.sum()))
 
 
-def test_unnormalised_weights(moe):
-    T, E, k = 513, 200, 6
+@pytest.mark.parametrize("E", [200, 64, 24, 100, 30])
+def test_unnormalised_weights(moe, E):
+    # E = 64 and 24 put 4 and 8 tokens in a wave, 100 and 30 two; T = 513
+    # leaves the last wave partly empty
+    T, k = 513, 6
     r = np.random.default_rng(2)
     logits = (2 * r.standard_normal((T, E))).astype(np.float32)
     say(f"unnormalised weights T={T} E={E} k={k}")
