@@ -27,13 +27,14 @@ MOE_ERR_WORKSPACE = 3
 MOE_ERR_LAUNCH = 4
 MOE_ROUTE_NORMALIZE = 1
 MOE_COMBINE_OUT_FP32 = 1
+MOE_FLOOR_NT_STORE = 1
 
 EXPORTS = ("moe_route_topk", "moe_route_topk_grouped", "moe_layout_workspace_size", "moe_dispatch_layout",
            "moe_dispatch_permute", "moe_combine_reduce", "moe_fp8_row_bytes",
            "moe_dispatch_permute_fp8", "moe_fp8_dequant", "moe_recv_regroup_workspace_size",
            "moe_recv_regroup_layout", "moe_recv_regroup", "moe_recv_ungroup",
            "moe_expert_linear_workspace_size", "moe_expert_linear", "moe_expert_linear_return",
-           "moe_expert_return_slots", "moe_status_string")
+           "moe_expert_return_slots", "moe_hbm_floor", "moe_status_string")
 
 
 class MoeError(RuntimeError):
@@ -54,10 +55,10 @@ def _load_library() -> ctypes.CDLL:
     lib.moe_layout_workspace_size.argtypes = [i64, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.moe_dispatch_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P,
                                         ctypes.c_size_t, P]
-    lib.moe_dispatch_permute.argtypes = [P, P, i64, i32, i32, P, i64, P]
+    lib.moe_dispatch_permute.argtypes = [P, P, i64, i32, i32, i32, i32, P, i64, P]
     lib.moe_combine_reduce.argtypes = [P, i64, P, P, P, P, i64, i32, i32, u32, P, P]
     lib.moe_fp8_row_bytes.argtypes = [i32, ctypes.POINTER(ctypes.c_int64)]
-    lib.moe_dispatch_permute_fp8.argtypes = [P, P, i64, i32, i32, P, i64, P]
+    lib.moe_dispatch_permute_fp8.argtypes = [P, P, i64, i32, i32, i32, i32, P, i64, P]
     lib.moe_fp8_dequant.argtypes = [P, P, i64, i32, P, P]
     lib.moe_recv_regroup_workspace_size.argtypes = [i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.moe_recv_regroup_layout.argtypes = [P, i32, i32, P, P, P, i64, P, ctypes.c_size_t, P]
@@ -68,6 +69,7 @@ def _load_library() -> ctypes.CDLL:
     lib.moe_expert_linear_return.argtypes = [P, P, i32, i32, i32, i32, P, i64, i32, i32, i32, P, P, P,
                                              ctypes.c_size_t, P]
     lib.moe_expert_return_slots.argtypes = [ctypes.POINTER(ctypes.c_int32)]
+    lib.moe_hbm_floor.argtypes = [P, i64, P, i64, u32, P]
     lib.moe_status_string.argtypes = [ctypes.c_int]
     lib.moe_status_string.restype = ctypes.c_char_p
     for name in EXPORTS[:-1]:
@@ -189,17 +191,27 @@ def moe_dispatch_layout(topk_idx: torch.Tensor, E: int, R: int, capacity: int = 
     return o
 
 
-def moe_dispatch_permute(x: torch.Tensor, pos: torch.Tensor, send_rows: int,
-                         send: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
-    """send[pos[t, j]] = x[t] for every kept replica (see moe_dispatch_permute)."""
+def send_rows_bound(T: int, k: int, E: int, capacity: int = -1) -> int:
+    """Rows a send buffer needs: T*k when dropless, else min(T*k, E*capacity)."""
+    return T * k if capacity < 0 else min(T * k, E * capacity)
+
+
+def moe_dispatch_permute(x: torch.Tensor, pos: torch.Tensor, E: int, capacity: int = -1,
+                         send: Optional[torch.Tensor] = None, send_rows: Optional[int] = None,
+                         stream=None) -> torch.Tensor:
+    """send[pos[t, j]] = x[t] for every kept replica (see moe_dispatch_permute).
+    E and capacity are the layout's; send (allocated with the bound's rows when
+    not given) must hold at least send_rows_bound(T, k, E, capacity) rows."""
     T, H = x.shape
     k = pos.shape[1]
+    if send_rows is None:
+        send_rows = send.shape[0] if send is not None else send_rows_bound(T, k, E, capacity)
     if send is None:
         send = torch.empty((send_rows, H), dtype=x.dtype, device=x.device)
     if send.shape[0] < send_rows or (send.dim() == 2 and send.shape[1] != H):
         raise ValueError("send buffer smaller than send_rows x H")
     _check("moe_dispatch_permute", lib.moe_dispatch_permute(
-        _ptr(x, _BF16, "x", 2), _ptr(pos, _I32, "pos", 2), T, H, k,
+        _ptr(x, _BF16, "x", 2), _ptr(pos, _I32, "pos", 2), T, H, k, E, capacity,
         _ptr(send, _BF16, "send"), send_rows, _stream(stream)))
     return send
 
@@ -281,19 +293,23 @@ def moe_fp8_row_bytes(H: int) -> int:
     return n.value
 
 
-def moe_dispatch_permute_fp8(x: torch.Tensor, pos: torch.Tensor, send_rows: int,
-                             send: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+def moe_dispatch_permute_fp8(x: torch.Tensor, pos: torch.Tensor, E: int, capacity: int = -1,
+                             send: Optional[torch.Tensor] = None, send_rows: Optional[int] = None,
+                             stream=None) -> torch.Tensor:
     """FP8 send buffer [send_rows, moe_fp8_row_bytes(H)] uint8: row pos[t][j]
-    holds x[t]'s E4M3 codes then its scale bytes (see moe_dispatch_permute_fp8)."""
+    holds x[t]'s E4M3 codes then its scale bytes (see moe_dispatch_permute_fp8).
+    Rows as in moe_dispatch_permute."""
     T, H = x.shape
     k = pos.shape[1]
     rb = moe_fp8_row_bytes(H)
+    if send_rows is None:
+        send_rows = send.shape[0] if send is not None else send_rows_bound(T, k, E, capacity)
     if send is None:
         send = torch.empty((send_rows, rb), dtype=torch.uint8, device=x.device)
     elif send.dim() != 2 or send.shape[1] != rb or send.shape[0] < send_rows:
         raise ValueError(f"send must be [>= {send_rows}, {rb}] bytes, got {tuple(send.shape)}")
     _check("moe_dispatch_permute_fp8", lib.moe_dispatch_permute_fp8(
-        _ptr(x, _BF16, "x", 2), _ptr(pos, _I32, "pos", 2), T, H, k,
+        _ptr(x, _BF16, "x", 2), _ptr(pos, _I32, "pos", 2), T, H, k, E, capacity,
         _ptr(send, (torch.uint8,), "send", 2), send_rows, _stream(stream)))
     return send
 
@@ -367,3 +383,17 @@ def moe_expert_linear_return(recv: torch.Tensor, recv_counts: torch.Tensor, W: t
         _ptr(y, _BF16, "y", 2), _ptr(ret, _BF16, "ret", 2),
         _ptr(workspace, (torch.uint8,), "workspace"), workspace.numel(), _stream(stream)))
     return y, ret, workspace
+
+
+def moe_hbm_floor(src: torch.Tensor, read_bytes: int, dst: torch.Tensor, write_bytes: int,
+                  nt_store: bool = True, stream=None) -> None:
+    """The synthetic floor: a contiguous streaming read of read_bytes from src
+    and write of write_bytes to dst (see moe_hbm_floor)."""
+    if src.numel() * src.element_size() < read_bytes or dst.numel() * dst.element_size() < write_bytes:
+        raise ValueError("floor buffers smaller than the bytes to move")
+    for t, name in ((src, "src"), (dst, "dst")):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous GPU tensor")
+    _check("moe_hbm_floor", lib.moe_hbm_floor(
+        src.data_ptr() or None, read_bytes, dst.data_ptr() or None, write_bytes,
+        MOE_FLOOR_NT_STORE if nt_store else 0, _stream(stream)))

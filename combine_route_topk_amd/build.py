@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libmoe_ep.so")
 
-SOURCES = ["api.hip", "route_topk.hip", "layout.hip", "permute.hip", "combine.hip", "regroup.hip", "fp8.hip", "expert.hip"]
+SOURCES = ["api.hip", "route_topk.hip", "layout.hip", "permute.hip", "combine.hip", "regroup.hip", "fp8.hip", "expert.hip", "floor.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",

@@ -57,6 +57,26 @@ moe_status_t check_layout_sizes(int64_t T, int32_t E, int32_t k, int32_t R)
 
 moe_status_t from_hip(hipError_t err) { return err == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH; }
 
+// The permutes' sizes: the send buffer must hold every row the layout can
+// keep, T * k when dropless, else min(T * k, E * capacity).
+moe_status_t check_permute(int64_t T, int32_t H, int32_t k, int32_t E, int32_t capacity,
+                           int64_t send_rows)
+{
+    moe_status_t s = check_tokens(T, k);
+    if (s != MOE_OK)
+        return s;
+    if ((s = check_experts(E, k)) != MOE_OK)
+        return s;
+    if ((s = check_hidden(H)) != MOE_OK)
+        return s;
+    int64_t bound = T * (int64_t)k;
+    if (capacity >= 0 && (int64_t)E * capacity < bound)
+        bound = (int64_t)E * capacity;
+    if (send_rows < bound)
+        return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
 moe_status_t check_regroup_sizes(int32_t S, int32_t El)
 {
     if (S < 1 || El < 1)
@@ -179,15 +199,12 @@ moe_status_t moe_dispatch_layout(const int32_t *topk_idx, int64_t T, int32_t E, 
 }
 
 moe_status_t moe_dispatch_permute(const uint16_t *x, const int32_t *pos, int64_t T, int32_t H,
-                                  int32_t k, uint16_t *send, int64_t send_rows, void *stream)
+                                  int32_t k, int32_t E, int32_t capacity, uint16_t *send,
+                                  int64_t send_rows, void *stream)
 {
-    moe_status_t s = check_tokens(T, k);
+    moe_status_t s = check_permute(T, H, k, E, capacity, send_rows);
     if (s != MOE_OK)
         return s;
-    if ((s = check_hidden(H)) != MOE_OK)
-        return s;
-    if (send_rows < 0)
-        return MOE_ERR_INVALID_ARG;
     if (T == 0)
         return MOE_OK;
     if (!x || !pos || (!send && send_rows > 0))
@@ -212,18 +229,14 @@ moe_status_t moe_fp8_row_bytes(int32_t H, int64_t *bytes)
 }
 
 moe_status_t moe_dispatch_permute_fp8(const uint16_t *x, const int32_t *pos, int64_t T,
-                                      int32_t H, int32_t k, uint8_t *send, int64_t send_rows,
-                                      void *stream)
+                                      int32_t H, int32_t k, int32_t E, int32_t capacity,
+                                      uint8_t *send, int64_t send_rows, void *stream)
 {
-    moe_status_t s = check_tokens(T, k);
+    moe_status_t s = check_permute(T, H, k, E, capacity, send_rows);
     if (s != MOE_OK)
-        return s;
-    if ((s = check_hidden(H)) != MOE_OK)
         return s;
     if (H % 32 != 0)
         return MOE_ERR_UNSUPPORTED;
-    if (send_rows < 0)
-        return MOE_ERR_INVALID_ARG;
     if (T == 0)
         return MOE_OK;
     if (!x || !pos || (!send && send_rows > 0))
@@ -421,6 +434,20 @@ moe_status_t moe_expert_return_slots(int32_t *slots)
         return MOE_ERR_LAUNCH;
     *slots = n;
     return MOE_OK;
+}
+
+moe_status_t moe_hbm_floor(const void *src, int64_t read_bytes, void *dst, int64_t write_bytes,
+                           uint32_t flags, void *stream)
+{
+    if (read_bytes < 0 || write_bytes < 0 || read_bytes % 16 || write_bytes % 16 ||
+        (flags & ~MOE_FLOOR_NT_STORE))
+        return MOE_ERR_INVALID_ARG;
+    if ((read_bytes > 0 && (!src || !aligned(src, 16))) ||
+        (write_bytes > 0 && (!dst || !aligned(dst, 16))))
+        return MOE_ERR_INVALID_ARG;
+    return from_hip(moe::launch_hbm_floor(src, read_bytes, dst, write_bytes,
+                                          (flags & MOE_FLOOR_NT_STORE) != 0,
+                                          static_cast<hipStream_t>(stream)));
 }
 
 const char *moe_status_string(moe_status_t status)

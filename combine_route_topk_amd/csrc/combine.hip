@@ -33,12 +33,18 @@ __device__ __forceinline__ void add_bf16x8(float (&acc)[8], const u32x4 &v)
     }
 }
 
+// KMAX <= kExactK: the kernel is built for exactly k = KMAX replicas, so
+// each lane reserves registers for k rows and no more; above it KMAX is a
+// bound and k a run-time value.
+constexpr int kExactK = 16;
+
 template <int KMAX, bool OUT_F32>
 __global__ __launch_bounds__(kRowThreads) void combine_kernel(
     const u32x4 *__restrict__ y, int64_t y_rows, const int32_t *__restrict__ pos,
     const float *__restrict__ topk_w, const u32x4 *__restrict__ shared,
-    const u32x4 *__restrict__ residual, int32_t C16, int32_t k, void *__restrict__ out)
+    const u32x4 *__restrict__ residual, int32_t C16, int32_t k_arg, void *__restrict__ out)
 {
+    const int32_t k = KMAX <= kExactK ? KMAX : k_arg;
     const int64_t t = blockIdx.x;
     const int32_t c = blockIdx.y * kRowThreads + threadIdx.x;
     // the token's k positions and weights: lane j < k of each wave loads entry
@@ -120,17 +126,25 @@ hipError_t launch_kmax(const uint16_t *y, int64_t y_rows, const int32_t *pos, co
                        int32_t k, bool out_fp32, void *out, hipStream_t stream)
 {
     const int32_t C16 = H / 8;
-    const dim3 grid((unsigned)T, (unsigned)((C16 + kRowThreads - 1) / kRowThreads));
     const u32x4 *yv = reinterpret_cast<const u32x4 *>(y);
-    const u32x4 *sv = reinterpret_cast<const u32x4 *>(shared);
-    const u32x4 *rv = reinterpret_cast<const u32x4 *>(residual);
-    if (out_fp32)
-        hipLaunchKernelGGL((combine_kernel<KMAX, true>), grid, dim3(kRowThreads), 0, stream, yv,
-                           y_rows, pos, topk_w, sv, rv, C16, k, out);
-    else
-        hipLaunchKernelGGL((combine_kernel<KMAX, false>), grid, dim3(kRowThreads), 0, stream, yv,
-                           y_rows, pos, topk_w, sv, rv, C16, k, out);
-    return hipGetLastError();
+    // one block per token; past kMaxRowBlocks tokens, one launch per chunk
+    for (int64_t t0 = 0; t0 < T; t0 += kMaxRowBlocks) {
+        const int64_t n = T - t0 < kMaxRowBlocks ? T - t0 : kMaxRowBlocks;
+        const dim3 grid((unsigned)n, (unsigned)((C16 + kRowThreads - 1) / kRowThreads));
+        const u32x4 *sv = shared ? reinterpret_cast<const u32x4 *>(shared) + t0 * C16 : nullptr;
+        const u32x4 *rv = residual ? reinterpret_cast<const u32x4 *>(residual) + t0 * C16 : nullptr;
+        void *o = static_cast<char *>(out) + t0 * C16 * 16 * (out_fp32 ? 2 : 1);
+        if (out_fp32)
+            hipLaunchKernelGGL((combine_kernel<KMAX, true>), grid, dim3(kRowThreads), 0, stream,
+                               yv, y_rows, pos + t0 * k, topk_w + t0 * k, sv, rv, C16, k, o);
+        else
+            hipLaunchKernelGGL((combine_kernel<KMAX, false>), grid, dim3(kRowThreads), 0, stream,
+                               yv, y_rows, pos + t0 * k, topk_w + t0 * k, sv, rv, C16, k, o);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+    }
+    return hipSuccess;
 }
 
 }  // namespace
@@ -140,18 +154,22 @@ hipError_t launch_combine_reduce(const uint16_t *y, int64_t y_rows, const int32_
                                  const uint16_t *residual, int64_t T, int32_t H, int32_t k,
                                  bool out_fp32, void *out, hipStream_t stream)
 {
+    // one kernel per k up to 16: a kernel built for a bound above k keeps
+    // registers for rows it never loads (k = 10 under a bound of 16 took 79
+    // VGPRs and 6 waves per SIMD; built for exactly 10, 58 VGPRs and 8)
 #define MOE_COMBINE_ARGS y, y_rows, pos, topk_w, shared, residual, T, H, k, out_fp32, out, stream
-    if (k <= 1)
-        return launch_kmax<1>(MOE_COMBINE_ARGS);
-    if (k <= 2)
-        return launch_kmax<2>(MOE_COMBINE_ARGS);
-    if (k <= 4)
-        return launch_kmax<4>(MOE_COMBINE_ARGS);
-    if (k <= 8)
-        return launch_kmax<8>(MOE_COMBINE_ARGS);
-    if (k <= 16)
-        return launch_kmax<16>(MOE_COMBINE_ARGS);
-    return launch_kmax<32>(MOE_COMBINE_ARGS);
+#define MOE_COMBINE_K(n) \
+    case n:              \
+        return launch_kmax<n>(MOE_COMBINE_ARGS);
+    switch (k) {
+        MOE_COMBINE_K(1) MOE_COMBINE_K(2) MOE_COMBINE_K(3) MOE_COMBINE_K(4)
+        MOE_COMBINE_K(5) MOE_COMBINE_K(6) MOE_COMBINE_K(7) MOE_COMBINE_K(8)
+        MOE_COMBINE_K(9) MOE_COMBINE_K(10) MOE_COMBINE_K(11) MOE_COMBINE_K(12)
+        MOE_COMBINE_K(13) MOE_COMBINE_K(14) MOE_COMBINE_K(15) MOE_COMBINE_K(16)
+    default:
+        return launch_kmax<32>(MOE_COMBINE_ARGS);
+    }
+#undef MOE_COMBINE_K
 #undef MOE_COMBINE_ARGS
 }
 

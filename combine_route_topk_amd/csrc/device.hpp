@@ -11,6 +11,11 @@ namespace moe {
 
 constexpr int kWave = 64;
 
+// Row kernels launch one block per row (or token) and x-dimension; past this
+// many rows the grid is capped and blocks stride over the rest, which keeps
+// grid.x * 256 threads below 2^32.
+constexpr int64_t kMaxRowBlocks = (int64_t)1 << 22;
+
 __device__ __forceinline__ int lane_id() { return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)); }
 
 // 64-bit ballot of a predicate across the wave.

@@ -156,7 +156,6 @@ __global__ __launch_bounds__(kRowThreads) void fp8_dequant_kernel(
     }
 }
 
-constexpr int64_t kMaxRowBlocks = 1 << 22;  // keeps grid.x * 256 below 2^32
 
 }  // namespace
 
@@ -170,11 +169,18 @@ hipError_t launch_dispatch_permute_fp8(const uint16_t *x, const int32_t *pos, in
                                        hipStream_t stream)
 {
     const int32_t C32 = H / 16;
-    const dim3 grid((unsigned)T, (unsigned)((H + kSlabValues - 1) / kSlabValues));
-    hipLaunchKernelGGL(permute_fp8_kernel, grid, dim3(kRowThreads), 0, stream,
-                       reinterpret_cast<const u32x4 *>(x), pos, C32, k, send, send_rows,
-                       fp8_row_bytes(H));
-    return hipGetLastError();
+    // one block per token; past kMaxRowBlocks tokens, one launch per chunk
+    for (int64_t t0 = 0; t0 < T; t0 += kMaxRowBlocks) {
+        const int64_t n = T - t0 < kMaxRowBlocks ? T - t0 : kMaxRowBlocks;
+        const dim3 grid((unsigned)n, (unsigned)((H + kSlabValues - 1) / kSlabValues));
+        hipLaunchKernelGGL(permute_fp8_kernel, grid, dim3(kRowThreads), 0, stream,
+                           reinterpret_cast<const u32x4 *>(x) + t0 * C32 * 2, pos + t0 * k, C32,
+                           k, send, send_rows, fp8_row_bytes(H));
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_fp8_dequant(const uint8_t *rows, const int32_t *n_rows, int64_t max_rows,

@@ -87,4 +87,8 @@ hipError_t launch_regroup_rows(const uint16_t *src, const int32_t *map, const in
                                int64_t max_rows, int32_t H, bool gather, uint16_t *dst,
                                hipStream_t stream);
 
+// Synthetic floor: a contiguous streaming read and write (floor.hip).
+hipError_t launch_hbm_floor(const void *src, int64_t read_bytes, void *dst, int64_t write_bytes,
+                            bool nt_store, hipStream_t stream);
+
 }  // namespace moe

@@ -52,11 +52,18 @@ hipError_t launch_dispatch_permute(const uint16_t *x, const int32_t *pos, int64_
                                    hipStream_t stream)
 {
     const int32_t C16 = H / 8;
-    const dim3 grid((unsigned)T, (unsigned)((C16 + kRowThreads - 1) / kRowThreads));
-    hipLaunchKernelGGL(permute_kernel, grid, dim3(kRowThreads), 0, stream,
-                       reinterpret_cast<const u32x4 *>(x), pos, C16, k,
-                       reinterpret_cast<u32x4 *>(send), send_rows);
-    return hipGetLastError();
+    // one block per token; past kMaxRowBlocks tokens, one launch per chunk
+    for (int64_t t0 = 0; t0 < T; t0 += kMaxRowBlocks) {
+        const int64_t n = T - t0 < kMaxRowBlocks ? T - t0 : kMaxRowBlocks;
+        const dim3 grid((unsigned)n, (unsigned)((C16 + kRowThreads - 1) / kRowThreads));
+        hipLaunchKernelGGL(permute_kernel, grid, dim3(kRowThreads), 0, stream,
+                           reinterpret_cast<const u32x4 *>(x) + t0 * C16, pos + t0 * k, C16, k,
+                           reinterpret_cast<u32x4 *>(send), send_rows);
+        const hipError_t err = hipGetLastError();
+        if (err != hipSuccess)
+            return err;
+    }
+    return hipSuccess;
 }
 
 }  // namespace moe

@@ -34,7 +34,6 @@ constexpr int kTableThreads = 1024;
 constexpr int kPosThreads = 1024;
 constexpr int kPosRowsPerThread = 8;
 constexpr int kRowThreads = 256;
-constexpr int64_t kMaxRowBlocks = 1 << 22;  // keeps grid.x * 256 below 2^32
 
 // Exclusive scan of one value per thread over the block (1024 threads);
 // returns the thread's prefix and leaves the grand total in *total.

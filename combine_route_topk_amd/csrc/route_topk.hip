@@ -391,22 +391,33 @@ void launch_cand(const float *logits, const float *bias, int64_t T, int32_t E, i
                  float *topk_w, hipStream_t stream)
 {
     const int64_t per_block = (int64_t)kWavesPerBlock * TPW;
-    const dim3 grid((unsigned)((T + per_block - 1) / per_block));
+    // one wave per TPW tokens; past kMaxRowBlocks blocks, one launch per chunk
+    // of tokens (a loop inside the kernel cost it 20-30 VGPRs)
+    const int64_t chunk = kMaxRowBlocks * per_block;
+    for (int64_t t0 = 0; t0 < T; t0 += chunk) {
+        const int64_t n = T - t0 < chunk ? T - t0 : chunk;
+        const dim3 grid((unsigned)((n + per_block - 1) / per_block));
+        const float *lg = logits + t0 * E;
+        int32_t *ti = topk_idx + t0 * k;
+        float *tw = topk_w + t0 * k;
 #define MOE_ROUTE_LAUNCH(N, B)                                                                      \
     hipLaunchKernelGGL((route_topk_kernel<NSLOT, VEC, N, TPW, NC, B>), grid, dim3(kRouteThreads), 0, \
-                       stream, logits, bias, T, E, k, n_groups, topk_groups, topk_idx, topk_w)
-    if (normalize) {
-        if (bias)
-            MOE_ROUTE_LAUNCH(true, true);
-        else
-            MOE_ROUTE_LAUNCH(true, false);
-    } else {
-        if (bias)
-            MOE_ROUTE_LAUNCH(false, true);
-        else
-            MOE_ROUTE_LAUNCH(false, false);
-    }
+                       stream, lg, bias, n, E, k, n_groups, topk_groups, ti, tw)
+        if (normalize) {
+            if (bias)
+                MOE_ROUTE_LAUNCH(true, true);
+            else
+                MOE_ROUTE_LAUNCH(true, false);
+        } else {
+            if (bias)
+                MOE_ROUTE_LAUNCH(false, true);
+            else
+                MOE_ROUTE_LAUNCH(false, false);
+        }
 #undef MOE_ROUTE_LAUNCH
+        if (hipPeekAtLastError() != hipSuccess)
+            return;
+    }
 }
 
 template <int NSLOT, int VEC, int TPW>

@@ -193,18 +193,20 @@ moe_status_t moe_dispatch_layout(const int32_t *topk_idx, int64_t T,
  * Arguments:
  *   x         [T][H] bf16, 16-byte aligned.
  *   pos       [T][k] int32 from moe_dispatch_layout (-1 = dropped).
- *   send      [send_rows][H] bf16 out, 16-byte aligned. Rows that no
- *             replica points at are not written. send_rows must cover N
- *             (T * k when dropless, min(T * k, E * capacity) otherwise);
- *             positions >= send_rows are skipped (a broken precondition,
- *             never a write out of bounds).
- * Errors: MOE_ERR_INVALID_ARG for NULL/misaligned pointers, T < 0,
- *   send_rows < 0; MOE_ERR_UNSUPPORTED outside the limits.
+ *   E, capacity  the expert count and capacity given to moe_dispatch_layout;
+ *             they fix the bound on the kept rows N: T * k when dropless
+ *             (capacity < 0), min(T * k, E * capacity) otherwise.
+ *   send      [send_rows][H] bf16 out, 16-byte aligned, send_rows >= that
+ *             bound. Rows that no replica points at are not written.
+ *             Positions >= send_rows (a broken precondition on pos) are
+ *             skipped, never written out of bounds.
+ * Errors: MOE_ERR_INVALID_ARG for NULL/misaligned pointers, T < 0, or
+ *   send_rows below the bound; MOE_ERR_UNSUPPORTED outside the limits.
  */
 moe_status_t moe_dispatch_permute(const uint16_t *x, const int32_t *pos,
-                                  int64_t T, int32_t H, int32_t k,
-                                  uint16_t *send, int64_t send_rows,
-                                  void *stream);
+                                  int64_t T, int32_t H, int32_t k, int32_t E,
+                                  int32_t capacity, uint16_t *send,
+                                  int64_t send_rows, void *stream);
 
 /*
  * moe_combine_reduce -- bring each token's k expert outputs back along the
@@ -275,12 +277,13 @@ moe_status_t moe_fp8_row_bytes(int32_t H, int64_t *bytes);
  * moe_dispatch_permute_fp8 -- as moe_dispatch_permute, but row pos[t][j] of
  * send ([send_rows][moe_fp8_row_bytes(H)] bytes, 16-byte aligned) receives
  * the FP8 codes, scale bytes and zero padding of x[t]. Rows no kept
- * assignment points at are left as they were.
+ * assignment points at are left as they were. send_rows must cover the
+ * same bound as in moe_dispatch_permute.
  * Errors: as moe_dispatch_permute; MOE_ERR_UNSUPPORTED when H % 32 != 0.
  */
 moe_status_t moe_dispatch_permute_fp8(const uint16_t *x, const int32_t *pos, int64_t T,
-                                      int32_t H, int32_t k, uint8_t *send,
-                                      int64_t send_rows, void *stream);
+                                      int32_t H, int32_t k, int32_t E, int32_t capacity,
+                                      uint8_t *send, int64_t send_rows, void *stream);
 
 /*
  * moe_fp8_dequant -- decode FP8 rows to bf16 (for an expert that takes
@@ -446,6 +449,31 @@ moe_status_t moe_expert_linear_return(const uint16_t *recv, const int32_t *recv_
 /* Blocks of one moe_expert_linear_return launch on the current device
  * (resident blocks per compute unit x compute units). */
 moe_status_t moe_expert_return_slots(int32_t *slots);
+
+/* moe_hbm_floor flags */
+#define MOE_FLOOR_NT_STORE 1u  /* stores carry the non-temporal hint */
+
+/*
+ * moe_hbm_floor -- the synthetic floor: read read_bytes from src and write
+ * write_bytes to dst, both contiguous, with the 16-byte lane accesses of
+ * the row kernels and nothing else (no gather, scatter or index). Timed
+ * beside a call of the path with that call's read and write volumes, it is
+ * the rate the memory system reaches for the same bytes; the gap is
+ * overhead the path owns.
+ *
+ * Defined by: aicassindra "gpu_moe_all_to_all", "How to tell whether the
+ * all-to-all is your bottleneck" (time a synthetic transfer of the same
+ * sizes and compare).
+ *
+ * Arguments: src [read_bytes], dst [write_bytes], 16-byte aligned, not
+ *   overlapping; sizes multiples of 16. dst receives the first write_bytes
+ *   of src (a constant pattern past read_bytes); the contents are not part
+ *   of the contract.
+ * Errors: MOE_ERR_INVALID_ARG for negative or unaligned sizes, NULL or
+ *   misaligned pointers with a non-zero size, or unknown flags.
+ */
+moe_status_t moe_hbm_floor(const void *src, int64_t read_bytes, void *dst,
+                           int64_t write_bytes, uint32_t flags, void *stream);
 
 /* moe_status_string -- a static, human-readable name for a status. */
 const char *moe_status_string(moe_status_t status);

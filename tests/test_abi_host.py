@@ -120,11 +120,24 @@ def test_layout_validation(moe):
 
 def test_permute_and_combine_validation(moe):
     lib = moe.lib
-    assert lib.moe_dispatch_permute(FAKE, FAKE, 4, 12, 2, FAKE, 8, None) == moe.MOE_ERR_UNSUPPORTED
-    assert lib.moe_dispatch_permute(FAKE, FAKE, 4, 16, 2, FAKE, -1, None) == moe.MOE_ERR_INVALID_ARG
-    assert lib.moe_dispatch_permute(FAKE + 4, FAKE, 4, 16, 2, FAKE, 8, None) == moe.MOE_ERR_INVALID_ARG
-    assert lib.moe_dispatch_permute(None, FAKE, 4, 16, 2, FAKE, 8, None) == moe.MOE_ERR_INVALID_ARG
-    assert lib.moe_dispatch_permute(None, None, 0, 16, 2, None, 0, None) == moe.MOE_OK
+    def perm(x=FAKE, pos=FAKE, T=4, H=16, k=2, E=8, C=-1, send=FAKE, rows=8):
+        return lib.moe_dispatch_permute(x, pos, T, H, k, E, C, send, rows, None)
+
+    assert perm(H=12) == moe.MOE_ERR_UNSUPPORTED
+    assert perm(rows=-1) == moe.MOE_ERR_INVALID_ARG
+    assert perm(x=FAKE + 4) == moe.MOE_ERR_INVALID_ARG
+    assert perm(x=None) == moe.MOE_ERR_INVALID_ARG
+    assert perm(x=None, pos=None, T=0, send=None, rows=0) == moe.MOE_OK
+    assert perm(E=0) == moe.MOE_ERR_UNSUPPORTED
+    assert perm(E=1) == moe.MOE_ERR_UNSUPPORTED            # k > E
+    assert perm(E=2048) == moe.MOE_ERR_UNSUPPORTED
+    # the send buffer must hold the bound on the kept rows: T*k dropless,
+    # min(T*k, E*capacity) with a capacity
+    assert perm(rows=7) == moe.MOE_ERR_INVALID_ARG
+    assert perm(C=0, rows=0, send=None, x=None, pos=None) == moe.MOE_ERR_INVALID_ARG  # pointers still required
+    assert perm(T=4096, k=8, E=64, C=100, rows=6399) == moe.MOE_ERR_INVALID_ARG     # bound 6400
+    assert perm(T=4096, k=8, E=64, C=1000, rows=32767) == moe.MOE_ERR_INVALID_ARG   # bound T*k
+    assert perm(T=2 ** 24, k=2, rows=2 ** 25 - 1) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_combine_reduce(FAKE, 8, FAKE, FAKE, None, None, 4, 16, 2, 2, FAKE, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_combine_reduce(FAKE, 8, FAKE, FAKE, None, None, 4, 0, 2, 0, FAKE, None) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_combine_reduce(FAKE, 8, FAKE, FAKE, MIS, None, 4, 16, 2, 0, FAKE, None) == moe.MOE_ERR_INVALID_ARG
@@ -193,8 +206,8 @@ def test_fp8_validation(moe):
     assert lib.moe_fp8_row_bytes(0, ctypes.byref(n)) == moe.MOE_ERR_UNSUPPORTED
     assert lib.moe_fp8_row_bytes(64, None) == moe.MOE_ERR_INVALID_ARG
 
-    def perm(x=FAKE, pos=FAKE, T=16, H=64, k=2, send=FAKE, rows=32):
-        return lib.moe_dispatch_permute_fp8(x, pos, T, H, k, send, rows, None)
+    def perm(x=FAKE, pos=FAKE, T=16, H=64, k=2, E=8, C=-1, send=FAKE, rows=32):
+        return lib.moe_dispatch_permute_fp8(x, pos, T, H, k, E, C, send, rows, None)
 
     assert perm(T=-1) == moe.MOE_ERR_INVALID_ARG
     assert perm(k=0) == moe.MOE_ERR_UNSUPPORTED
@@ -208,6 +221,9 @@ def test_fp8_validation(moe):
     assert perm(x=FAKE + 8) == moe.MOE_ERR_INVALID_ARG
     assert perm(send=FAKE + 8) == moe.MOE_ERR_INVALID_ARG
     assert perm(pos=MIS) == moe.MOE_ERR_INVALID_ARG
+    assert perm(rows=31) == moe.MOE_ERR_INVALID_ARG             # bound T*k = 32
+    assert perm(C=3, rows=23) == moe.MOE_ERR_INVALID_ARG        # bound E*C = 24
+    assert perm(E=1) == moe.MOE_ERR_UNSUPPORTED
 
     def deq(rows=FAKE, n=FAKE, max_rows=16, H=64, out=FAKE):
         return lib.moe_fp8_dequant(rows, n, max_rows, H, out, None)
@@ -266,6 +282,22 @@ def test_expert_linear_validation(moe):
     assert ret(group=0) == moe.MOE_ERR_INVALID_ARG
     assert ret(r=None) == moe.MOE_ERR_INVALID_ARG
     assert ret(r=FAKE + 8) == moe.MOE_ERR_INVALID_ARG
+
+
+def test_floor_validation(moe):
+    lib = moe.lib
+
+    def floor(src=FAKE, rb=1024, dst=FAKE, wb=1024, flags=1):
+        return lib.moe_hbm_floor(src, rb, dst, wb, flags, None)
+
+    assert floor(rb=-16) == moe.MOE_ERR_INVALID_ARG
+    assert floor(wb=-16) == moe.MOE_ERR_INVALID_ARG
+    assert floor(rb=1000) == moe.MOE_ERR_INVALID_ARG       # not a multiple of 16
+    assert floor(wb=24) == moe.MOE_ERR_INVALID_ARG
+    assert floor(flags=2) == moe.MOE_ERR_INVALID_ARG
+    assert floor(src=None) == moe.MOE_ERR_INVALID_ARG
+    assert floor(dst=FAKE + 8) == moe.MOE_ERR_INVALID_ARG
+    assert floor(src=None, rb=0, dst=None, wb=0) == moe.MOE_OK
 
 
 def test_binding_refuses_host_tensors(moe):

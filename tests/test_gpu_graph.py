@@ -61,7 +61,7 @@ def test_graph_replay_matches_eager(moe, cfg):
     def step():
         moe.moe_route_topk(logits, bias, w.k, topk_idx=idx, topk_w=wt, stream=s)
         moe.moe_dispatch_layout(idx, w.E, w.R, w.capacity, workspace=ws, out=L, stream=s)
-        moe.moe_dispatch_permute(x, L["pos"], rows, send=send, stream=s)
+        moe.moe_dispatch_permute(x, L["pos"], w.E, w.capacity, send=send, stream=s)
         moe.moe_combine_reduce(send, L["pos"], wt, sh, res, out=out, stream=s)
 
     torch.cuda.synchronize()

@@ -128,7 +128,7 @@ def test_dispatch_permute(moe, cfg):
     rows = send_rows_bound(w)
     say("dispatch_permute", w.describe(), f"N={N} send_rows={rows}")
     send = torch.full((rows, w.H), 0x5A5A, dtype=torch.int16, device=DEV).view(torch.bfloat16)
-    moe.moe_dispatch_permute(up(d["x"], True), up(ref["L"]["pos"]), rows, send=send)
+    moe.moe_dispatch_permute(up(d["x"], True), up(ref["L"]["pos"]), w.E, w.capacity, send=send)
     torch.cuda.synchronize()
     got = down_u16(send)
     np.testing.assert_array_equal(got[:N], ref["send"][:N])
@@ -165,7 +165,7 @@ def test_end_to_end(moe, cfg):
     x = up(d["x"], True)
     idx, wt = moe.moe_route_topk(up(d["logits"]), None if d["bias"] is None else up(d["bias"]), w.k)
     L = gpu_layout(moe, idx, w)
-    send = moe.moe_dispatch_permute(x, L["pos"], send_rows_bound(w))
+    send = moe.moe_dispatch_permute(x, L["pos"], w.E, w.capacity)
     out = moe.moe_combine_reduce(send, L["pos"], wt,
                                  None if d["shared"] is None else up(d["shared"], True),
                                  up(d["residual"], True))
@@ -210,7 +210,7 @@ def _run_small(moe, T, H, E, k, R, capacity=-1, seed=0, logits=None, bias=None, 
     L = moe.moe_dispatch_layout(idx, E, R, capacity)
     rows = T * k if capacity < 0 else min(T * k, E * capacity)
     send = torch.full((max(rows, 1), H), 0x1234, dtype=torch.int16, device=DEV).view(torch.bfloat16)
-    moe.moe_dispatch_permute(up(x, True), L["pos"], rows, send=send)
+    moe.moe_dispatch_permute(up(x, True), L["pos"], E, capacity, send=send)
     out = moe.moe_combine_reduce(send, L["pos"], wt, None if sh is None else up(sh, True), up(res, True))
     torch.cuda.synchronize()
     got = dict(idx=idx.cpu().numpy(), w=wt.cpu().numpy(), send=down_u16(send), out=down_u16(out),
@@ -331,7 +331,7 @@ def test_zero_tokens(moe, E):
     k, R, H = 2, 4, 64
     idx, wt = moe.moe_route_topk(torch.empty((0, E), device=DEV), None, k)
     L = moe.moe_dispatch_layout(idx, E, R, -1)
-    send = moe.moe_dispatch_permute(torch.empty((0, H), dtype=torch.bfloat16, device=DEV), L["pos"], 0)
+    send = moe.moe_dispatch_permute(torch.empty((0, H), dtype=torch.bfloat16, device=DEV), L["pos"], E)
     out = moe.moe_combine_reduce(send, L["pos"], wt)
     torch.cuda.synchronize()
     assert out.shape == (0, H)
@@ -355,17 +355,21 @@ def test_invalid_ids_are_ignored(moe):
     assert np.array_equal(np.sort(pos[ok]), np.arange(ok.sum()))
 
 
-@pytest.mark.parametrize("E", [200, 64, 24, 100, 30])
-def test_unnormalised_weights(moe, E):
-    # E = 64 and 24 put 4 and 8 tokens in a wave, 100 and 30 two; T = 513
-    # leaves the last wave partly empty
-    T, k = 513, 6
+@pytest.mark.parametrize("E,k,biased", [(200, 6, False), (64, 6, False), (24, 6, False), (100, 6, False),
+                                        (30, 6, False), (16, 4, False), (16, 3, True), (64, 6, True),
+                                        (512, 10, True), (30, 5, True)])
+def test_unnormalised_weights(moe, E, k, biased):
+    # E = 16 (k <= 4), 24 and 64 put 16, 8 and 4 tokens in a wave, 100 and 30
+    # two; T = 513 leaves the last wave partly empty. With a selection bias
+    # the weights still come from the unbiased logits.
+    T = 513
     r = np.random.default_rng(2)
     logits = (2 * r.standard_normal((T, E))).astype(np.float32)
-    say(f"unnormalised weights T={T} E={E} k={k}")
-    idx, wt = moe.moe_route_topk(up(logits), None, k, normalize=False)
+    bias = r.uniform(-0.5, 0.5, E).astype(np.float32) if biased else None
+    say(f"unnormalised weights T={T} E={E} k={k} bias={biased}")
+    idx, wt = moe.moe_route_topk(up(logits), None if bias is None else up(bias), k, normalize=False)
     torch.cuda.synchronize()
-    o_idx, o_w = oracle.route_topk(logits, None, k, normalize=False)
+    o_idx, o_w = oracle.route_topk(logits, bias, k, normalize=False)
     np.testing.assert_array_equal(idx.cpu().numpy(), o_idx)
     # full softmax over E: the sum has E terms
     d = np.abs(logits.astype(np.float64).max(axis=1, keepdims=True)
@@ -374,51 +378,128 @@ def test_unnormalised_weights(moe, E):
     assert np.all(np.abs(wt.cpu().numpy() - o_w) <= tol)
 
 
-def test_reproducible(moe):
-    w = synthetic.WORKLOADS[3]
-    d = inputs(3)
+@pytest.mark.parametrize("cfg", CONFIGS)
+def test_reproducible(moe, cfg):
+    """Two runs of the whole path give the same bits: ids, weights, layout,
+    send rows, and the combined rows in bf16 and in fp32."""
+    w = synthetic.WORKLOADS[cfg]
+    d = inputs(cfg)
     say("reproducible", w.describe())
+    sh = None if d["shared"] is None else up(d["shared"], True)
     outs = []
     for _ in range(2):
-        idx, wt = moe.moe_route_topk(up(d["logits"]), None, w.k)
+        idx, wt = moe.moe_route_topk(up(d["logits"]), None if d["bias"] is None else up(d["bias"]), w.k)
         L = gpu_layout(moe, idx, w)
-        send = moe.moe_dispatch_permute(up(d["x"], True), L["pos"], send_rows_bound(w))
-        out = moe.moe_combine_reduce(send, L["pos"], wt, None, up(d["residual"], True))
+        send = moe.moe_dispatch_permute(up(d["x"], True), L["pos"], w.E, w.capacity)
+        out = moe.moe_combine_reduce(send, L["pos"], wt, sh, up(d["residual"], True))
+        out32 = moe.moe_combine_reduce(send, L["pos"], wt, sh, up(d["residual"], True), out_fp32=True)
         torch.cuda.synchronize()
         N = int(L["expert_offsets"][-1].item())
         # send_src entries at and past N are never written
-        outs.append([t.cpu() for t in (idx, wt, L["pos"], L["send_src"][:N], send[:N], out)])
+        outs.append([t.cpu() for t in (idx, wt, L["expert_counts"], L["expert_offsets"], L["pos"],
+                                       L["send_src"][:N], send[:N], out, out32)])
     for a, b in zip(*outs):
         assert np.array_equal(a.contiguous().view(torch.uint8).numpy(), b.contiguous().view(torch.uint8).numpy())
 
 
-def _lane_experts(E, lane):
-    """Experts whose logits one lane of the route kernel holds: runs of four
-    (4l..4l+3, then +256) with 16-byte loads (E % 4 == 0), else l + 64i."""
+@pytest.mark.parametrize("cfg,capacity", [(1, -1), (1, 20), (2, -1), (2, 3), (3, 615)])
+def test_layout_paths_agree(moe, cfg, capacity):
+    """The one-block layout (at most 4096 assignments, E <= 512) and the tiled
+    two-pass layout give the same counts, offsets, positions and send rows
+    for the same assignments: the ids are laid out once with the workload's
+    E and again with E' = 1024 experts, which takes the tiled path (experts
+    past E receive nothing). The capacity-limited workload (32768
+    assignments) goes the other way: a first slice of its tokens fits the
+    one-block path."""
+    w = synthetic.WORKLOADS[cfg]
+    d = inputs(cfg)
+    o_idx, _ = oracle.route_topk(d["logits"], d["bias"], w.k)
+    if w.T * w.k > 4096:
+        o_idx = o_idx[:4096 // w.k]
+    T, E = o_idx.shape[0], w.E
+    say(f"layout paths agree {w.name} T={T} C={capacity}")
+    assert T * w.k <= 4096 and moe.moe_layout_workspace_size(T, E, w.k, w.R) == 0
+    assert moe.moe_layout_workspace_size(T, 1024, w.k, 1) > 0
+    small = moe.moe_dispatch_layout(up(o_idx), E, w.R, capacity)
+    tiled = moe.moe_dispatch_layout(up(o_idx), 1024, 1, capacity)
+    torch.cuda.synchronize()
+    ref = oracle.dispatch_layout(o_idx, E, w.R, capacity)
+    N = int(ref["expert_offsets"][-1])
+    for name, n in (("expert_demand", E), ("expert_counts", E), ("expert_offsets", E + 1)):
+        np.testing.assert_array_equal(small[name].cpu().numpy()[:n], ref[name][:n], err_msg=name)
+        np.testing.assert_array_equal(tiled[name].cpu().numpy()[:n], ref[name][:n], err_msg=name)
+    assert np.all(tiled["expert_counts"].cpu().numpy()[E:] == 0)
+    assert np.all(tiled["expert_offsets"].cpu().numpy()[E:] == N)
+    for L in (small, tiled):
+        np.testing.assert_array_equal(L["pos"].cpu().numpy(), ref["pos"])
+        np.testing.assert_array_equal(L["send_src"][:N].cpu().numpy(), ref["send_src"][:N])
+
+
+def _lanes_per_token(E, k, n_groups=0):
+    """Lanes of one token in the route kernel, by the launcher's rule (rows
+    16-byte aligned): with 16-byte loads (E % 4 == 0) a token takes the
+    smallest power of two >= 4 lanes that holds its row in runs of four, its
+    k ids and one lane per group, while that is at most 16 (4, 8 or 16
+    tokens per wave); else 32 lanes for rows of at most 128 experts (32 with
+    4-byte loads) and at most 32 groups; else the whole wave."""
+    vec4 = E % 4 == 0
+    seg = 4
+    while seg < (E + 3) // 4 or seg < k or seg < n_groups:
+        seg *= 2
+    if vec4 and seg <= 16:
+        return seg
+    if (E <= 128 if vec4 else E <= 32) and n_groups <= 32:
+        return 32
+    return 64
+
+
+def _lane_experts(E, gl, hw):
+    """Experts whose logits in-token lane gl holds when a token has hw lanes:
+    runs of four (4gl..4gl+3, then + 4hw) with 16-byte loads (E % 4 == 0),
+    else gl + hw*i."""
     if E % 4 == 0:
-        ids = [256 * q + 4 * lane + c for q in range((E + 255) // 256) for c in range(4)]
+        ids = [4 * hw * q + 4 * gl + c for q in range((E + 4 * hw - 1) // (4 * hw)) for c in range(4)]
     else:
-        ids = [lane + 64 * i for i in range((E + 63) // 64)]
+        ids = [gl + hw * i for i in range((E + hw - 1) // hw)]
     return np.array([e for e in ids if e < E], dtype=np.int64)
 
 
+def test_lane_model():
+    """The lane model above against the tokens-per-wave cases the launcher
+    documents: 16, 8 and 4 tokens per wave for E <= 16, 32 and 64 with 16-byte
+    loads, two for E <= 128, one above; k and the group count can widen it."""
+    assert _lanes_per_token(16, 4) == 4 and _lanes_per_token(16, 5) == 8
+    assert _lanes_per_token(32, 8) == 8 and _lanes_per_token(64, 8) == 16
+    assert _lanes_per_token(64, 17) == 32 and _lanes_per_token(128, 16) == 32
+    assert _lanes_per_token(512, 10) == 64 and _lanes_per_token(30, 6) == 32
+    assert _lanes_per_token(100, 7) == 32 and _lanes_per_token(32, 5, 16) == 16
+    # every expert is held by exactly one in-token lane
+    for E, hw in ((512, 64), (64, 16), (30, 32), (100, 32), (16, 4), (902, 64)):
+        got = np.sort(np.concatenate([_lane_experts(E, gl, hw) for gl in range(hw)]))
+        np.testing.assert_array_equal(got, np.arange(E))
+
+
 @pytest.mark.parametrize("E,k", [(512, 10), (512, 3), (512, 2), (1024, 32), (1024, 1), (300, 16),
-                                 (902, 5), (902, 2), (64, 8), (128, 16), (100, 7), (30, 6)])
+                                 (902, 5), (902, 2), (64, 8), (128, 16), (100, 7), (30, 6),
+                                 (32, 6), (32, 8), (16, 3), (16, 4), (64, 12)])
 def test_route_candidate_rescans(moe, E, k):
     """Rows that make one lane win round after round (so it must refill its
     candidates from its registers, possibly several times), rows of ties and
     special values, and all-equal rows: on row widths whose lanes hold 8 or
-    more slots (three candidates when k >= 3), and on rows of at most 128
-    experts, where each 32-lane half of a wave routes its own token."""
+    more slots (three candidates when k >= 3), on rows of at most 128
+    experts, where each 32-lane half of a wave routes its own token, and on
+    rows of 16 to 64 experts, where 16, 8 or 4 tokens share a wave. The
+    planted winner sits on a lane inside the token's own lanes."""
     T = 1024
     r = np.random.default_rng(E * 100 + k)
     pool = np.array([0.0, -0.0, 1.0, -1.0, 0.5, 2.0, np.inf, -np.inf, np.nan], np.float32)
     logits = r.choice(pool, size=(T, E)).astype(np.float32)        # rows 0, 4, ...: ties everywhere
     logits[1::4] = r.standard_normal((len(range(1, T, 4)), E), dtype=np.float32)
     top = r.standard_normal((len(range(2, T, 4)), E), dtype=np.float32) - 10.0
-    two = (E <= 128) if E % 4 == 0 else (E <= 32)                    # 32 lanes per token
+    hw = _lanes_per_token(E, k)
+    lanes = [gl for gl in range(hw) if _lane_experts(E, gl, hw).size]   # lanes past the row hold padding
     for n, row in enumerate(range(2, T, 4)):
-        ids = _lane_experts(E, n % (32 if two else 64))              # one lane holds the best
+        ids = _lane_experts(E, lanes[n % len(lanes)], hw)           # one lane holds the best
         top[n, ids] = 10.0 + r.standard_normal(len(ids), dtype=np.float32)
         if n % 2:
             top[n, ids[::2]] = 10.0                                  # with exact ties inside it
@@ -468,7 +549,9 @@ GROUPED = [
     (333, 70, 6, 7, 2, "uniform"),     # 4-byte route path
     (200, 64, 4, 64, 4, None),         # one expert per group: plain top-k
     (300, 64, 6, 8, 8, None),          # every group allowed: plain top-k
-    (777, 32, 5, 16, 3, "uniform"),    # two tokens per wave, 16-byte loads, odd T
+    (777, 32, 5, 16, 3, "uniform"),    # 16 groups need 16 lanes: four tokens per wave, odd T
+    (901, 32, 4, 8, 3, "uniform"),     # eight tokens per wave, 16-byte loads, odd T
+    (555, 16, 3, 4, 2, None),          # sixteen tokens per wave
     (401, 30, 4, 5, 2, None),          # two tokens per wave, 4-byte loads, odd T
 ]
 
@@ -491,7 +574,8 @@ def test_route_topk_grouped(moe, case):
     assert np.all(np.abs(wt.cpu().numpy() - o_w)[finite] <= tol[finite])
 
 
-@pytest.mark.parametrize("E,k,G,M", [(512, 10, 8, 4), (1024, 12, 16, 3), (384, 8, 64, 4), (120, 6, 8, 3)])
+@pytest.mark.parametrize("E,k,G,M", [(512, 10, 8, 4), (1024, 12, 16, 3), (384, 8, 64, 4), (120, 6, 8, 3),
+                                     (64, 8, 8, 3), (32, 6, 8, 4)])
 def test_route_grouped_ties_and_specials(moe, E, k, G, M):
     """Group-limited routing on rows full of ties, signed zeros, infinities
     and NaNs (group maxima tie too), on rows where one lane holds the best
@@ -502,9 +586,10 @@ def test_route_grouped_ties_and_specials(moe, E, k, G, M):
     pool = np.array([0.0, -0.0, 1.0, -1.0, 2.0, np.inf, -np.inf, np.nan], np.float32)
     logits = r.choice(pool, size=(T, E)).astype(np.float32)
     logits[1::3] = r.standard_normal((len(range(1, T, 3)), E), dtype=np.float32) - 10.0
-    two = (E <= 128) if E % 4 == 0 else (E <= 32)
+    hw = _lanes_per_token(E, k, G)
+    lanes = [gl for gl in range(hw) if _lane_experts(E, gl, hw).size]
     for n, row in enumerate(range(1, T, 3)):
-        ids = _lane_experts(E, n % (32 if two else 64))
+        ids = _lane_experts(E, lanes[n % len(lanes)], hw)
         logits[row, ids] = 10.0 + np.round(r.standard_normal(len(ids)), 1).astype(np.float32)
     logits[2::3] = 0.0
     bias = np.where(r.random(E) < 0.5, 0.0, 1.0).astype(np.float32)   # ties survive the bias

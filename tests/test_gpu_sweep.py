@@ -91,7 +91,7 @@ def test_random_path(moe, case):
         idx, wt = moe.moe_route_topk_grouped(up(logits), up(bias), k, *groups)
     L = moe.moe_dispatch_layout(idx, E, R, capacity)
     rows = T * k if capacity < 0 else min(T * k, E * capacity)
-    send = moe.moe_dispatch_permute(up_bf16(x), L["pos"], max(rows, 1))
+    send = moe.moe_dispatch_permute(up_bf16(x), L["pos"], E, capacity, send_rows=max(rows, 1))
     out = moe.moe_combine_reduce(send, L["pos"], wt, up_bf16(sh), up_bf16(res))
     torch.cuda.synchronize()
 
