@@ -30,6 +30,7 @@ MOE_COMBINE_OUT_FP32 = 1
 MOE_FLOOR_NT_STORE = 1
 
 EXPORTS = ("moe_route_topk", "moe_route_topk_grouped", "moe_layout_workspace_size", "moe_dispatch_layout",
+           "moe_dispatch_layout_noalloc",
            "moe_dispatch_permute", "moe_combine_reduce", "moe_fp8_row_bytes",
            "moe_dispatch_permute_fp8", "moe_fp8_dequant", "moe_recv_regroup_workspace_size",
            "moe_recv_regroup_layout", "moe_recv_regroup", "moe_recv_ungroup",
@@ -55,6 +56,7 @@ def _load_library() -> ctypes.CDLL:
     lib.moe_layout_workspace_size.argtypes = [i64, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.moe_dispatch_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P,
                                         ctypes.c_size_t, P]
+    lib.moe_dispatch_layout_noalloc.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P]
     lib.moe_dispatch_permute.argtypes = [P, P, i64, i32, i32, i32, i32, P, i64, P]
     lib.moe_combine_reduce.argtypes = [P, i64, P, P, P, P, i64, i32, i32, u32, P, P]
     lib.moe_fp8_row_bytes.argtypes = [i32, ctypes.POINTER(ctypes.c_int64)]
@@ -188,6 +190,28 @@ def moe_dispatch_layout(topk_idx: torch.Tensor, E: int, R: int, capacity: int = 
         _ptr(o["dest_offsets"], _I32, "dest_offsets"), _ptr(o["pos"], _I32, "pos"),
         _ptr(o["send_src"], _I32, "send_src"), _ptr(workspace, (torch.uint8,), "workspace"),
         workspace.numel(), _stream(stream)))
+    return o
+
+
+def moe_dispatch_layout_noalloc(topk_idx: torch.Tensor, E: int, R: int, capacity: int = -1,
+                                out: Optional[dict] = None, with_send_src: bool = True,
+                                stream=None) -> dict:
+    """moe_dispatch_layout without a workspace (see moe_dispatch_layout_noalloc):
+    the library's own per-GPU device array holds the tile histograms. Outputs
+    as moe_dispatch_layout; missing ones are allocated here, by torch."""
+    T, k = topk_idx.shape
+    dev = topk_idx.device
+    o = dict(out or {})
+    shapes = {"expert_demand": (E,), "expert_counts": (E,), "expert_offsets": (E + 1,),
+              "dest_counts": (R,), "dest_offsets": (R + 1,), "pos": (T, k), "send_src": (T * k,)}
+    for name, shape in shapes.items():
+        if name == "send_src" and not with_send_src:
+            o[name] = None
+        elif o.get(name) is None:
+            o[name] = torch.empty(shape, dtype=torch.int32, device=dev)
+    _check("moe_dispatch_layout_noalloc", lib.moe_dispatch_layout_noalloc(
+        _ptr(topk_idx, _I32, "topk_idx", 2), T, E, k, R, capacity,
+        *[_ptr(o[n], _I32, n) for n in shapes], _stream(stream)))
     return o
 
 

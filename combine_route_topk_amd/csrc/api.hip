@@ -198,6 +198,34 @@ moe_status_t moe_dispatch_layout(const int32_t *topk_idx, int64_t T, int32_t E, 
         static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_dispatch_layout_noalloc(const int32_t *topk_idx, int64_t T, int32_t E, int32_t k,
+                                         int32_t R, int32_t capacity, int32_t *expert_demand,
+                                         int32_t *expert_counts, int32_t *expert_offsets,
+                                         int32_t *dest_counts, int32_t *dest_offsets,
+                                         int32_t *pos, int32_t *send_src, void *stream)
+{
+    moe_status_t s = check_layout_sizes(T, E, k, R);
+    if (s != MOE_OK)
+        return s;
+    if ((T > 0 && (!topk_idx || !pos)) || !expert_demand || !expert_counts || !expert_offsets ||
+        !dest_counts || !dest_offsets)
+        return MOE_ERR_INVALID_ARG;
+    const void *ptrs[] = {topk_idx,     expert_demand, expert_counts, expert_offsets,
+                          dest_counts, dest_offsets,  pos,           send_src};
+    for (const void *p : ptrs)
+        if (!aligned(p, 4))
+            return MOE_ERR_INVALID_ARG;
+    const size_t need = moe::layout_workspace_bytes(T * (int64_t)k, E);
+    if (need > moe::layout_scratch_bytes())
+        return MOE_ERR_WORKSPACE;
+    int32_t *scratch = nullptr;
+    if (need > 0 && moe::layout_scratch(&scratch) != hipSuccess)
+        return MOE_ERR_LAUNCH;
+    return from_hip(moe::launch_dispatch_layout(
+        topk_idx, T, E, k, R, capacity, expert_demand, expert_counts, expert_offsets, dest_counts,
+        dest_offsets, pos, send_src, scratch, static_cast<hipStream_t>(stream)));
+}
+
 moe_status_t moe_dispatch_permute(const uint16_t *x, const int32_t *pos, int64_t T, int32_t H,
                                   int32_t k, int32_t E, int32_t capacity, uint16_t *send,
                                   int64_t send_rows, void *stream)

@@ -42,6 +42,11 @@ inline size_t layout_workspace_bytes(int64_t TK, int32_t E)
     return (size_t)layout_plan(TK, E).tiles * (size_t)E * sizeof(int32_t);
 }
 
+// The allocation-free layout's device array (layout.hip): its size, and its
+// address on the current device (looked up once per device).
+size_t layout_scratch_bytes();
+hipError_t layout_scratch(int32_t **ptr);
+
 hipError_t launch_dispatch_layout(const int32_t *topk_idx, int64_t T, int32_t E, int32_t k,
                                   int32_t R, int32_t capacity, int32_t *expert_demand,
                                   int32_t *expert_counts, int32_t *expert_offsets,

@@ -34,8 +34,21 @@
 //    over 16 waves (8 when E > 512). Block 0 publishes counts and offsets.
 #include "device.hpp"
 #include "launch.hpp"
+#include "moe_ep.h"
+
+#include <atomic>
 
 namespace moe {
+
+// Workspace of the allocation-free entry point: one E-wide int32 histogram
+// per tile, for every legal size (at most kMaxTiles tiles of at most 1024
+// experts, 512 KiB). Each GPU the library runs on holds its own copy until
+// the process ends. In host code this name is only a handle: the array's
+// device address comes from hipGetSymbolAddress, once per device.
+constexpr int64_t kScratchInts = kMaxTiles * 1024;
+static __device__ __align__(256) int32_t scratch[kScratchInts];
+static_assert(sizeof(scratch) == MOE_LAYOUT_SCRATCH_BYTES, "the header states the array's size");
+
 namespace {
 
 constexpr int kSmallThreads = 1024;
@@ -430,6 +443,32 @@ hipError_t launch_dispatch_layout(const int32_t *topk_idx, int64_t T, int32_t E,
                            pos, send_src);
     }
     return hipGetLastError();
+}
+
+size_t layout_scratch_bytes() { return sizeof(scratch); }
+
+hipError_t layout_scratch(int32_t **ptr)
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int32_t *> by_device[kMaxDevices];
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return err;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    int32_t *p = by_device[dev].load(std::memory_order_acquire);
+    if (p == nullptr) {
+        // first call on this device (with it current): two threads may both
+        // ask, and both get the same address
+        void *addr = nullptr;
+        if ((err = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch))) != hipSuccess)
+            return err;
+        p = static_cast<int32_t *>(addr);
+        by_device[dev].store(p, std::memory_order_release);
+    }
+    *ptr = p;
+    return hipSuccess;
 }
 
 }  // namespace moe

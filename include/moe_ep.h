@@ -180,6 +180,31 @@ moe_status_t moe_dispatch_layout(const int32_t *topk_idx, int64_t T,
                                  size_t workspace_bytes, void *stream);
 
 /*
+ * moe_dispatch_layout_noalloc -- moe_dispatch_layout with no workspace
+ * argument, for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.
+ * Same arguments (minus workspace), outputs and errors. The call allocates
+ * nothing: the per-tile histograms live in a device array of
+ * MOE_LAYOUT_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; every legal size fits (sizes whose
+ * moe_layout_workspace_size() exceeds it would return MOE_ERR_WORKSPACE).
+ * All calls on one GPU share that array, and every call rewrites what it
+ * reads, so nothing carries over from the previous call; calls that overlap
+ * on one GPU (different streams, host threads) race on it and must be
+ * serialised by the caller. MOE_ERR_LAUNCH also covers a failure to look
+ * up the array's device address (once per device, on the first call).
+ */
+#define MOE_LAYOUT_SCRATCH_BYTES (128u * 1024u * 4u)
+moe_status_t moe_dispatch_layout_noalloc(const int32_t *topk_idx, int64_t T,
+                                         int32_t E, int32_t k, int32_t R,
+                                         int32_t capacity, int32_t *expert_demand,
+                                         int32_t *expert_counts,
+                                         int32_t *expert_offsets,
+                                         int32_t *dest_counts,
+                                         int32_t *dest_offsets, int32_t *pos,
+                                         int32_t *send_src, void *stream);
+
+/*
  * moe_dispatch_permute -- pack each kept replica of each token into its
  * send row: send[pos[t][j]][:] = x[t][:] (a bit copy of the bf16 row).
  *
