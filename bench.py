@@ -1,9 +1,11 @@
 """Benchmark of the MoE dispatch/combine core on one MI355X.
 
 One step = the whole path over one synthetic batch already resident in HBM:
-moe_route_topk -> moe_dispatch_layout -> moe_dispatch_permute ->
-moe_combine_reduce (the expert is the identity: combine reads the send
-buffer). W untimed warm-up steps, then exactly K timed steps between
+moe_route_dispatch_layout (routing and layout; one launch for batches of at
+most 4096 assignments) -> moe_dispatch_permute -> moe_combine_reduce (the
+expert is the identity: combine reads the send buffer). The same step with
+moe_route_topk and moe_dispatch_layout as separate calls is timed beside it
+("four_call_step_us"). W untimed warm-up steps, then exactly K timed steps between
 device synchronisations with HIP events only at the two ends (an event
 between calls leaves the GPU idle for a few microseconds). The steps are
 eager launches, each call's device pointers bound once before timing (as a
@@ -156,6 +158,11 @@ def rw_bytes(w, N, T_read, has_bias):
     }
 
 
+def call_bytes(nbytes, name):
+    """Algorithmic bytes of one call (route_layout: the two calls' bytes)."""
+    return nbytes["route"] + nbytes["layout"] if name == "route_layout" else nbytes[name]
+
+
 def algorithmic_bytes(w, N, T_read, has_bias):
     return {n: r + wr for n, (r, wr) in rw_bytes(w, N, T_read, has_bias).items()}
 
@@ -253,6 +260,17 @@ def summarize(directory):
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
         print(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
               f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
+    # the floor kernel runs at several byte mixes under one name: split by grid
+    trace = [r for r in _csv_rows(directory, "kernel_trace.csv") if _short(r["Kernel_Name"]).startswith("floor_kernel")]
+    if trace:
+        by = {}
+        for r in trace:
+            by.setdefault((_short(r["Kernel_Name"]), int(r["Grid_Size_X"])), []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        print("\n| floor launch | grid (threads) | calls | average us |")
+        print("|---|---|---|---|")
+        for (name, grid), v in sorted(by.items()):
+            print(f"| `{name}` | {grid} | {len(v)} | {sum(v) / len(v):.2f} |")
 
 
 def _counter_means(directory, counter):
@@ -343,13 +361,16 @@ class Step:
                         "expert_offsets": torch.empty(E + 1, **i32), "dest_counts": torch.empty(R, **i32),
                         "dest_offsets": torch.empty(R + 1, **i32), "pos": torch.empty((T, k), **i32),
                         "send_src": torch.empty(T * k, **i32)},
-                "ws": torch.empty(max(self.moe.moe_layout_workspace_size(T, E, k, R), 16), dtype=torch.uint8,
+                "ws": torch.zeros(self.moe.moe_route_dispatch_layout_workspace_size(T, E, k, R), dtype=torch.uint8,
                                   device=dev),
                 "send": torch.empty((self.send_rows, H), dtype=torch.bfloat16, device=dev),
                 "out": torch.empty((T, H), dtype=torch.bfloat16, device=dev)}
 
-    def calls(self, sp, o=None):
-        """The four calls with every pointer bound once (as a C caller holds them)."""
+    def calls(self, sp, o=None, fused=True):
+        """The step's calls with every pointer bound once (as a C caller holds
+        them): routing and layout in one call (moe_route_dispatch_layout: one
+        launch for small batches) unless fused is False or routing is
+        group-limited, then the permute and the combine."""
         o = self.main if o is None else o
         moe, lib, w = self.moe, self.moe.lib, self.w
         T, H, E, k, R, C = w.T, w.H, w.E, w.k, w.R, w.capacity
@@ -371,9 +392,14 @@ class Step:
         else:
             route = lambda: check("route", lib.moe_route_topk_grouped(logits, bias, T, E, k, g[0], g[1], norm,
                                                                       idx, wt, sp))
-        return [
-            ("route", route),
-            ("layout", lambda: check("layout", lib.moe_dispatch_layout(idx, T, E, k, R, C, *ld, ws, wsn, sp))),
+        if fused and g is None:
+            first = [("route_layout", lambda: check("route_layout", lib.moe_route_dispatch_layout(
+                logits, bias, T, E, k, norm, R, C, idx, wt, *ld, ws, wsn, sp)))]
+        else:
+            first = [("route", route),
+                     ("layout", lambda: check("layout", lib.moe_dispatch_layout(idx, T, E, k, R, C, *ld, ws, wsn,
+                                                                                sp)))]
+        return first + [
             ("permute", lambda: check("permute", lib.moe_dispatch_permute(x, pos, T, H, k, E, C, send, rows,
                                                                           sp))),
             ("combine", lambda: check("combine", lib.moe_combine_reduce(send, rows, pos, wt, sh, res, T, H, k, 0,
@@ -477,6 +503,10 @@ def measure_path(moe, torch, w, args, groups=None, full=True):
                 "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": stored_traffic(kname, w.name),
                 "kernel": kname, "algorithmic_bytes": nbytes[dominant],
                 "avg_launch_us": round(pc[dominant] * 1e3, 2)}
+    # the same step with routing and layout as two separate calls
+    calls4 = st.calls(stream.cuda_stream, fused=False)
+    ms_four = timed(torch, stream, lambda: [fn() for _, fn in calls4], args.steps, args.warmup)
+    pc4 = per_call_ms(torch, stream, calls4, args.steps)
     res = {"workload": w.describe(), "T": T, "H": H, "E": E, "k": k, "R": w.R, "capacity": w.capacity,
            "shared_expert": w.shared, "kept_rows": N, "tokens_read": T_read, "bytes_per_step": total,
            "us_per_step": round(ms_per_step * 1e3, 2), "GBps": round(gbps, 1),
@@ -484,7 +514,9 @@ def measure_path(moe, torch, w, args, groups=None, full=True):
            "tokens_per_s": round(T / (ms_per_step * 1e-3), 1),
            "host_us_per_step": round(wall_eager * 1e6, 1),
            "per_call_us": {n: round(v * 1e3, 2) for n, v in pc.items()},
-           "per_call_GBps": {n: round(nbytes[n] / (pc[n] * 1e-3) / 1e9, 1) for n in nbytes},
+           "per_call_GBps": {n: round(call_bytes(nbytes, n) / (v * 1e-3) / 1e9, 1) for n, v in pc.items()},
+           "four_call_step_us": round(ms_four * 1e3, 2),
+           "four_call_per_call_us": {n: round(v * 1e3, 2) for n, v in pc4.items()},
            "roofline": roofline}
     if ms_graph is not None:
         res["us_per_step_eager"] = round(ms_eager * 1e3, 2)
@@ -650,13 +682,13 @@ def bench_fp8(moe, torch, st, calls, nbytes, stream, warmup, steps):
         if rc != moe.MOE_OK:
             raise RuntimeError(f"{name}: {moe.moe_status_string(rc)}")
 
-    fcalls = calls[:2] + [
+    fcalls = [c for c in calls if c[0] not in ("permute", "combine")] + [
         ("permute_fp8", lambda: check("permute_fp8", lib.moe_dispatch_permute_fp8(
             x, pos, T, H, k, E, C, s8, rows, sp))),
         ("combine", lambda: check("combine", lib.moe_combine_reduce(
             yp, rows, pos, wt, sh, res, T, H, k, 0, op, sp))),
     ]
-    for _, fn in fcalls[:3]:
+    for _, fn in fcalls[:-1]:
         fn()
     check("fp8 dequant", lib.moe_fp8_dequant(s8, P(lay["expert_offsets"][E:]), rows, H, yp, sp))
     ms_step = timed(torch, stream, lambda: [fn() for _, fn in fcalls], steps, warmup)
@@ -679,6 +711,32 @@ def bench_fp8(moe, torch, st, calls, nbytes, stream, warmup, steps):
                       "identity expert's bf16 output, decoded once before timing"}
     log("fp8 dispatch", report)
     return report
+
+
+def token_ready_profile(cnt, pos, self_rank=0, band_rows=128, marks=(0.5, 0.75, 0.9, 0.99)):
+    """When each token's rows are all computed in the tile-signalled GEMM's
+    work order: bands of 128 rows of each (source, local expert) block, the
+    sources remote-first (self_rank + 1, ..., self_rank last), experts
+    ascending. Returns the share of tokens with a kept row whose last band is
+    among the first q of all bands, for each q in marks: the part of the
+    combine that could start before the GEMM ends."""
+    S, El = cnt.shape
+    starts = np.concatenate([[0], np.cumsum(cnt.ravel())])
+    band_of_row = np.empty(int(starts[-1]), np.int64)
+    b = 0
+    for s in [(self_rank + i) % S for i in range(1, S + 1)]:
+        for l in range(El):
+            n, r0 = int(cnt[s, l]), int(starts[s * El + l])
+            band_of_row[r0:r0 + n] = b + np.arange(n) // band_rows
+            b += (n + band_rows - 1) // band_rows
+    kept = pos >= 0
+    has = kept.any(axis=1)
+    if b == 0 or not has.any():
+        return {"bands": b, "tokens": 0}
+    last = np.where(kept, band_of_row[np.where(kept, pos, 0)], -1).max(axis=1)[has]
+    frac = (last + 1) / b
+    return {"bands": b, "tokens": int(has.sum()),
+            "share_ready_by_band_share": {str(q): round(float((frac <= q).mean()), 4) for q in marks}}
 
 
 def bench_tile_return(moe, torch, st, stream, warmup, steps, seed=0):
@@ -721,6 +779,7 @@ def bench_tile_return(moe, torch, st, stream, warmup, steps, seed=0):
            "roofline": {"bound": "mfma", "kernel": "expert_linear_kernel", "achieved": round(tflops, 1),
                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4), "flops": flops},
+           "token_ready_profile": token_ready_profile(cnt.cpu().numpy(), lay["pos"].cpu().numpy()),
            "note": "stand-in expert: one bf16 H x H linear map per local expert; band_group 2"}
     log("tile-signalled return", out)
     return out
@@ -814,7 +873,11 @@ def main(argv=None):
         "timing": "one HIP graph replay per step (four launches)" if args.graph else "eager launches",
         "ms_per_step_eager": round(ms_eager, 5),
         "host_us_per_step": r["host_us_per_step"],
-        "per_call_note": "second pass of the same K steps with an event pair around every call",
+        "per_call_note": ("second pass of the same K steps with an event pair around every call; "
+                          "route_layout is moe_route_dispatch_layout (one launch when T*k <= 4096 and "
+                          "E <= 512, else the routing and layout kernels)"),
+        "four_call_step_us": r["four_call_step_us"],
+        "four_call_per_call_us": r["four_call_per_call_us"],
         "per_call_GBps": r["per_call_GBps"],
         "step_us_spread": r.get("step_us_spread"),
         "step_us_spread_note": "third pass of K steps with one event between consecutive steps",

@@ -30,7 +30,7 @@ MOE_COMBINE_OUT_FP32 = 1
 MOE_FLOOR_NT_STORE = 1
 
 EXPORTS = ("moe_route_topk", "moe_route_topk_grouped", "moe_layout_workspace_size", "moe_dispatch_layout",
-           "moe_dispatch_layout_noalloc",
+           "moe_route_dispatch_layout_workspace_size", "moe_route_dispatch_layout", "moe_dispatch_layout_noalloc",
            "moe_dispatch_permute", "moe_combine_reduce", "moe_fp8_row_bytes",
            "moe_dispatch_permute_fp8", "moe_fp8_dequant", "moe_recv_regroup_workspace_size",
            "moe_recv_regroup_layout", "moe_recv_regroup", "moe_recv_ungroup",
@@ -56,6 +56,9 @@ def _load_library() -> ctypes.CDLL:
     lib.moe_layout_workspace_size.argtypes = [i64, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
     lib.moe_dispatch_layout.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P,
                                         ctypes.c_size_t, P]
+    lib.moe_route_dispatch_layout_workspace_size.argtypes = [i64, i32, i32, i32, ctypes.POINTER(ctypes.c_size_t)]
+    lib.moe_route_dispatch_layout.argtypes = [P, P, i64, i32, i32, u32, i32, i32, P, P, P, P, P, P, P, P, P, P,
+                                              ctypes.c_size_t, P]
     lib.moe_dispatch_layout_noalloc.argtypes = [P, i64, i32, i32, i32, i32, P, P, P, P, P, P, P, P]
     lib.moe_dispatch_permute.argtypes = [P, P, i64, i32, i32, i32, i32, P, i64, P]
     lib.moe_combine_reduce.argtypes = [P, i64, P, P, P, P, i64, i32, i32, u32, P, P]
@@ -189,6 +192,45 @@ def moe_dispatch_layout(topk_idx: torch.Tensor, E: int, R: int, capacity: int = 
         _ptr(o["expert_offsets"], _I32, "expert_offsets"), _ptr(o["dest_counts"], _I32, "dest_counts"),
         _ptr(o["dest_offsets"], _I32, "dest_offsets"), _ptr(o["pos"], _I32, "pos"),
         _ptr(o["send_src"], _I32, "send_src"), _ptr(workspace, (torch.uint8,), "workspace"),
+        workspace.numel(), _stream(stream)))
+    return o
+
+
+def moe_route_dispatch_layout_workspace_size(T: int, E: int, k: int, R: int) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_route_dispatch_layout_workspace_size",
+           lib.moe_route_dispatch_layout_workspace_size(T, E, k, R, ctypes.byref(n)))
+    return n.value
+
+
+def moe_route_dispatch_layout(logits: torch.Tensor, bias: Optional[torch.Tensor], k: int, R: int,
+                              capacity: int = -1, normalize: bool = True,
+                              workspace: Optional[torch.Tensor] = None, out: Optional[dict] = None,
+                              with_send_src: bool = True, stream=None) -> dict:
+    """moe_route_topk then moe_dispatch_layout in one call (see
+    moe_route_dispatch_layout). Returns the layout dict of moe_dispatch_layout
+    plus topk_idx [T,k] and topk_w [T,k]; `out` may hold any of them."""
+    T, E = logits.shape
+    dev = logits.device
+    o = dict(out or {})
+    shapes = {"topk_idx": (T, k), "expert_demand": (E,), "expert_counts": (E,), "expert_offsets": (E + 1,),
+              "dest_counts": (R,), "dest_offsets": (R + 1,), "pos": (T, k), "send_src": (T * k,)}
+    for name, shape in shapes.items():
+        if name == "send_src" and not with_send_src:
+            o[name] = None
+        elif o.get(name) is None:
+            o[name] = torch.empty(shape, dtype=torch.int32, device=dev)
+    if o.get("topk_w") is None:
+        o["topk_w"] = torch.empty((T, k), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(moe_route_dispatch_layout_workspace_size(T, E, k, R), dtype=torch.uint8,
+                                device=dev)
+    lay = [_ptr(o[n], _I32, n) for n in ("expert_demand", "expert_counts", "expert_offsets", "dest_counts",
+                                         "dest_offsets", "pos", "send_src")]
+    _check("moe_route_dispatch_layout", lib.moe_route_dispatch_layout(
+        _ptr(logits, _F32, "logits", 2), _ptr(bias, _F32, "bias", 1), T, E, k,
+        MOE_ROUTE_NORMALIZE if normalize else 0, R, capacity, _ptr(o["topk_idx"], _I32, "topk_idx"),
+        _ptr(o["topk_w"], _F32, "topk_w"), *lay, _ptr(workspace, (torch.uint8,), "workspace"),
         workspace.numel(), _stream(stream)))
     return o
 

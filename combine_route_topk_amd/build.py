@@ -19,7 +19,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB_PATH = os.path.join(PKG, "libmoe_ep.so")
 
-SOURCES = ["api.hip", "route_topk.hip", "layout.hip", "permute.hip", "combine.hip", "regroup.hip", "fp8.hip", "expert.hip", "floor.hip"]
+SOURCES = ["api.hip", "route_topk.hip", "layout.hip", "permute.hip", "combine.hip", "regroup.hip", "fp8.hip", "expert.hip", "floor.hip", "route_layout.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -54,5 +54,45 @@ def build(verbose: bool = False) -> str:
     return LIB_PATH
 
 
+def resource_usage(sources=None):
+    """Per-kernel resources the compiler reports for gfx950 (VGPRs, AGPRs,
+    SGPRs, LDS bytes, waves per SIMD), as (source, kernel, fields) rows."""
+    import re
+    rows = []
+    for src in sources or SOURCES:
+        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", os.devnull,
+               "-Rpass-analysis=kernel-resource-usage"]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            sys.stderr.write(r.stderr)
+            raise RuntimeError(f"hipcc failed on {src}")
+        cur = None
+        for line in r.stderr.splitlines():
+            m = re.search(r"remark: +Function Name: (\S+)", line)
+            if m:
+                cur = {"kernel": m.group(1)}
+                rows.append((src, cur))
+                continue
+            m = re.search(r"remark: +([A-Za-z ]+?)(?: \[[^]]*\])?: (\d+)", line)
+            if m and cur is not None:
+                cur[m.group(1).strip()] = int(m.group(2))
+    return rows
+
+
+def _demangle(names):
+    r = subprocess.run(["c++filt"], input="\n".join(names), capture_output=True, text=True)
+    return r.stdout.splitlines() if r.returncode == 0 else names
+
+
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--resource-usage" in sys.argv:
+        rows = resource_usage()
+        names = _demangle([f["kernel"] for _, f in rows])
+        print("| source | kernel | VGPRs | AGPRs | SGPRs | LDS bytes | waves per SIMD |")
+        print("|---|---|---|---|---|---|---|")
+        for (src, f), name in zip(rows, names):
+            name = name.replace("moe::(anonymous namespace)::", "").replace("void ", "").split("(")[0]
+            print(f"| {src} | `{name}` | {f.get('VGPRs')} | {f.get('AGPRs')} | {f.get('TotalSGPRs')} | "
+                  f"{f.get('LDS Size')} | {f.get('Occupancy')} |")
+    else:
+        print(build(verbose=True))

@@ -198,6 +198,49 @@ moe_status_t moe_dispatch_layout(const int32_t *topk_idx, int64_t T, int32_t E, 
         static_cast<hipStream_t>(stream)));
 }
 
+moe_status_t moe_route_dispatch_layout_workspace_size(int64_t T, int32_t E, int32_t k, int32_t R,
+                                                      size_t *bytes)
+{
+    if (!bytes)
+        return MOE_ERR_INVALID_ARG;
+    moe_status_t s = check_layout_sizes(T, E, k, R);
+    if (s != MOE_OK)
+        return s;
+    *bytes = moe::route_layout_workspace_bytes(T * (int64_t)k, E);
+    return MOE_OK;
+}
+
+moe_status_t moe_route_dispatch_layout(const float *logits, const float *bias, int64_t T,
+                                       int32_t E, int32_t k, uint32_t flags, int32_t R,
+                                       int32_t capacity, int32_t *topk_idx, float *topk_w,
+                                       int32_t *expert_demand, int32_t *expert_counts,
+                                       int32_t *expert_offsets, int32_t *dest_counts,
+                                       int32_t *dest_offsets, int32_t *pos, int32_t *send_src,
+                                       void *workspace, size_t workspace_bytes, void *stream)
+{
+    moe_status_t s = check_layout_sizes(T, E, k, R);
+    if (s != MOE_OK)
+        return s;
+    if (flags & ~MOE_ROUTE_NORMALIZE)
+        return MOE_ERR_INVALID_ARG;
+    if ((T > 0 && (!logits || !topk_idx || !topk_w || !pos)) || !expert_demand ||
+        !expert_counts || !expert_offsets || !dest_counts || !dest_offsets)
+        return MOE_ERR_INVALID_ARG;
+    const void *ptrs[] = {logits,         bias,        topk_idx,     topk_w,
+                          expert_demand,  expert_counts, expert_offsets, dest_counts,
+                          dest_offsets,   pos,         send_src};
+    for (const void *p : ptrs)
+        if (!aligned(p, 4))
+            return MOE_ERR_INVALID_ARG;
+    if (!workspace || !aligned(workspace, 16) ||
+        workspace_bytes < moe::route_layout_workspace_bytes(T * (int64_t)k, E))
+        return MOE_ERR_WORKSPACE;
+    return from_hip(moe::launch_route_layout(
+        logits, bias, T, E, k, (flags & MOE_ROUTE_NORMALIZE) != 0, R, capacity, topk_idx, topk_w,
+        expert_demand, expert_counts, expert_offsets, dest_counts, dest_offsets, pos, send_src,
+        workspace, static_cast<hipStream_t>(stream)));
+}
+
 moe_status_t moe_dispatch_layout_noalloc(const int32_t *topk_idx, int64_t T, int32_t E, int32_t k,
                                          int32_t R, int32_t capacity, int32_t *expert_demand,
                                          int32_t *expert_counts, int32_t *expert_offsets,

@@ -53,6 +53,22 @@ hipError_t launch_dispatch_layout(const int32_t *topk_idx, int64_t T, int32_t E,
                                   int32_t *dest_counts, int32_t *dest_offsets, int32_t *pos,
                                   int32_t *send_src, int32_t *tile_hist, hipStream_t stream);
 
+// Routing and layout in one call (route_layout.hip): one launch for small
+// batches, else the two kernels. The workspace starts with the fused
+// kernel's ticket word; the tiled layout's histograms follow.
+constexpr size_t kRouteLayoutHeaderBytes = 16;
+inline size_t route_layout_workspace_bytes(int64_t TK, int32_t E)
+{
+    return kRouteLayoutHeaderBytes + layout_workspace_bytes(TK, E);
+}
+bool route_layout_fuses(int64_t T, int32_t E, int32_t k, const float *logits, const float *bias);
+hipError_t launch_route_layout(const float *logits, const float *bias, int64_t T, int32_t E,
+                               int32_t k, bool normalize, int32_t R, int32_t capacity,
+                               int32_t *topk_idx, float *topk_w, int32_t *expert_demand,
+                               int32_t *expert_counts, int32_t *expert_offsets,
+                               int32_t *dest_counts, int32_t *dest_offsets, int32_t *pos,
+                               int32_t *send_src, void *workspace, hipStream_t stream);
+
 hipError_t launch_dispatch_permute(const uint16_t *x, const int32_t *pos, int64_t T, int32_t H,
                                    int32_t k, uint16_t *send, int64_t send_rows,
                                    hipStream_t stream);

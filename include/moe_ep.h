@@ -180,6 +180,50 @@ moe_status_t moe_dispatch_layout(const int32_t *topk_idx, int64_t T,
                                  size_t workspace_bytes, void *stream);
 
 /*
+ * moe_route_dispatch_layout -- moe_route_topk followed by
+ * moe_dispatch_layout (no group limit), in one call: the same outputs, bit
+ * for bit, with fewer launches for small batches.
+ *
+ * Defined by: the two calls' passages above, and aicassindra
+ * "gpu_moe_all_to_all", "Latency-bound at decode, bandwidth-bound at
+ * prefill" (at decode sizes the exchange is bound by latency: cut the
+ * independent steps and synchronisation points, not the bytes).
+ *
+ * When T * k <= 4096, E <= 512, E % 4 == 0 and logits and bias are 16-byte
+ * aligned, one kernel launch does both: its blocks route their tokens, and
+ * the last block to finish (an atomic ticket in the first 16 bytes of the
+ * workspace; no block waits for another) builds the layout from the ids the
+ * others wrote. Otherwise the call launches the routing and the layout
+ * kernels as the two separate calls do.
+ *
+ * Arguments: those of moe_route_topk (logits, bias, flags, topk_idx,
+ *   topk_w) and of moe_dispatch_layout (R, capacity and its outputs), plus
+ *   workspace  device memory of at least
+ *              moe_route_dispatch_layout_workspace_size() bytes (16 or
+ *              more), 16-byte aligned. Its contents on entry do not matter:
+ *              a call on a workspace its predecessor did not leave ready
+ *              counts arrivals with a slower, stamp-keyed protocol, and
+ *              every call leaves it ready. Calls that overlap in time must
+ *              not share a workspace.
+ * Errors: those of the two calls; MOE_ERR_WORKSPACE when the workspace is
+ *   NULL, misaligned or too small.
+ */
+moe_status_t moe_route_dispatch_layout_workspace_size(int64_t T, int32_t E,
+                                                      int32_t k, int32_t R,
+                                                      size_t *bytes);
+moe_status_t moe_route_dispatch_layout(const float *logits, const float *bias,
+                                       int64_t T, int32_t E, int32_t k,
+                                       uint32_t flags, int32_t R,
+                                       int32_t capacity, int32_t *topk_idx,
+                                       float *topk_w, int32_t *expert_demand,
+                                       int32_t *expert_counts,
+                                       int32_t *expert_offsets,
+                                       int32_t *dest_counts,
+                                       int32_t *dest_offsets, int32_t *pos,
+                                       int32_t *send_src, void *workspace,
+                                       size_t workspace_bytes, void *stream);
+
+/*
  * moe_dispatch_layout_noalloc -- moe_dispatch_layout with no workspace
  * argument, for callers that cannot allocate device memory: code under HIP
  * graph capture, tight serving loops, harnesses that forbid allocation.

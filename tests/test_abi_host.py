@@ -284,6 +284,39 @@ def test_expert_linear_validation(moe):
     assert ret(r=FAKE + 8) == moe.MOE_ERR_INVALID_ARG
 
 
+def test_route_layout_validation(moe):
+    lib = moe.lib
+    # the ticket word, then the tiled layout's histograms when there are any
+    assert moe.moe_route_dispatch_layout_workspace_size(100, 64, 2, 8) == 16
+    assert moe.moe_route_dispatch_layout_workspace_size(8192, 64, 8, 8) == 16 + 32768
+    n = ctypes.c_size_t(0)
+    assert lib.moe_route_dispatch_layout_workspace_size(4, 16, 2, 3, ctypes.byref(n)) == moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_route_dispatch_layout_workspace_size(4, 16, 2, 4, None) == moe.MOE_ERR_INVALID_ARG
+
+    def call(lg=FAKE, b=None, T=100, E=64, k=2, flags=1, R=8, C=-1, idx=FAKE, w=FAKE, out=FAKE, pos=FAKE,
+             ws=FAKE, wsb=16):
+        return lib.moe_route_dispatch_layout(lg, b, T, E, k, flags, R, C, idx, w, out, out, out, out, out, pos,
+                                             None, ws, wsb, None)
+
+    assert call(T=-1) == moe.MOE_ERR_INVALID_ARG
+    assert call(k=0) == moe.MOE_ERR_UNSUPPORTED
+    assert call(k=33, E=64) == moe.MOE_ERR_UNSUPPORTED
+    assert call(E=2048) == moe.MOE_ERR_UNSUPPORTED
+    assert call(R=3) == moe.MOE_ERR_INVALID_ARG
+    assert call(flags=2) == moe.MOE_ERR_INVALID_ARG
+    assert call(lg=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(idx=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(w=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(pos=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(out=None) == moe.MOE_ERR_INVALID_ARG
+    assert call(lg=MIS) == moe.MOE_ERR_INVALID_ARG
+    assert call(b=MIS) == moe.MOE_ERR_INVALID_ARG
+    assert call(ws=None) == moe.MOE_ERR_WORKSPACE
+    assert call(ws=FAKE + 8) == moe.MOE_ERR_WORKSPACE
+    assert call(wsb=15) == moe.MOE_ERR_WORKSPACE
+    assert call(T=8192, k=8, wsb=16 + 32767) == moe.MOE_ERR_WORKSPACE
+
+
 def test_floor_validation(moe):
     lib = moe.lib
 

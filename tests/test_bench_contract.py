@@ -96,3 +96,15 @@ def test_load_balance_hand_case(bench):
                    "dest_rows_max_over_mean": 2.0, "hot_dest_rows": 5, "dropped": 3}
     assert bench.load_balance(np.zeros(4, np.int32), np.zeros(4, np.int32), np.zeros(2, np.int32))[
         "expert_demand_max_over_mean"] is None
+
+
+def test_token_ready_profile_hand_case(bench):
+    """Two sources, two local experts, one-row bands: the work order is
+    source 1 (expert 0: row 2; expert 1: rows 3-5), then source 0 (rows 0-1),
+    so the tokens' last bands are 4, 1 and 3 of 6."""
+    import numpy as np
+    cnt = np.array([[2, 0], [1, 3]])
+    pos = np.array([[0, 2], [3, -1], [4, 5], [-1, -1]])
+    got = bench.token_ready_profile(cnt, pos, band_rows=1, marks=(0.5, 0.7, 1.0))
+    assert got == {"bands": 6, "tokens": 3,
+                   "share_ready_by_band_share": {"0.5": round(1 / 3, 4), "0.7": round(2 / 3, 4), "1.0": 1.0}}
