@@ -41,7 +41,8 @@ gap between a call and its floor is overhead the path owns.
 After the path, further measurements are reported under "next_rows", none
 part of `value`:
   * the same step with the FP8 dispatch payload (moe_dispatch_permute_fp8 in
-    place of the bf16 permute);
+    place of the bf16 permute), on this workload and on each prefill workload
+    under --also;
   * the receive-side regroup on the same buffers (the send buffer read as R
     source segments);
   * the tile-signalled return: a stand-in expert GEMM on those segments whose
@@ -260,17 +261,26 @@ def summarize(directory):
     for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
         print(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
               f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
-    # the floor kernel runs at several byte mixes under one name: split by grid
-    trace = [r for r in _csv_rows(directory, "kernel_trace.csv") if _short(r["Kernel_Name"]).startswith("floor_kernel")]
-    if trace:
-        by = {}
-        for r in trace:
-            by.setdefault((_short(r["Kernel_Name"]), int(r["Grid_Size_X"])), []).append(
-                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-        print("\n| floor launch | grid (threads) | calls | average us |")
+    # the floor kernel runs at several byte mixes under one name, one pass
+    # after another (the benchmark's order: step, permute, combine,
+    # write-only): split it into its passes, a pass being a run of launches
+    # with one grid that no other floor launch interrupts
+    trace = sorted(_csv_rows(directory, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
+    passes = []
+    for r in trace:
+        if not _short(r["Kernel_Name"]).startswith("floor_kernel"):
+            continue
+        grid = int(r["Grid_Size_X"])
+        if not passes or passes[-1][0] != grid:
+            passes.append((grid, []))
+        passes[-1][1].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    if passes:
+        names = ["step", "permute", "combine", "write-only"]
+        print("\n| floor pass (benchmark order) | grid (threads) | calls | average us |")
         print("|---|---|---|---|")
-        for (name, grid), v in sorted(by.items()):
-            print(f"| `{name}` | {grid} | {len(v)} | {sum(v) / len(v):.2f} |")
+        for i, (grid, v) in enumerate(passes):
+            label = names[i % 4] if len(passes) % 4 == 0 else str(i)
+            print(f"| {label} | {grid} | {len(v)} | {sum(v) / len(v):.2f} |")
 
 
 def _counter_means(directory, counter):
@@ -830,11 +840,14 @@ def main(argv=None):
         wx = workload_by_name(name)
         if wx.name == w.name:
             continue
-        rx, stx, _, _ = measure_path(moe, torch, wx, args, groups, full=False)
+        rx, stx, _, cx = measure_path(moe, torch, wx, args, groups, full=False)
+        if wx.name in PREFILL and not args.no_fp8 and wx.H % 32 == 0:
+            nbx = algorithmic_bytes(wx, rx["kept_rows"], rx["tokens_read"], stx.bias is not None)
+            rx["fp8_dispatch"] = bench_fp8(moe, torch, stx, cx, nbx, stream, args.warmup, args.steps)
         if wx.name in PREFILL and not args.no_tile_return and wx.R >= 2 and wx.H % 128 == 0:
             rx["tile_signalled_return"] = bench_tile_return(moe, torch, stx, stream, args.warmup, args.steps)
         workloads[wx.name] = rx
-        del stx
+        del stx, cx
         torch.cuda.empty_cache()
     if "tile_signalled_return" in next_rows:
         by = {w.name: next_rows["tile_signalled_return"]["signalled_vs_sequential"]}

@@ -605,3 +605,69 @@ def test_route_grouped_ties_and_specials(moe, E, k, G, M):
         if b is None:
             # all-equal rows: groups 0..M-1 tie and win, and inside them the lowest ids
             assert np.all(o_idx[2::3] == np.arange(k))
+
+
+# ---------------------------------------------------------------------------
+# token counts past the grid's limit: the launchers split the work
+# ---------------------------------------------------------------------------
+
+MAX_ROW_BLOCKS = 1 << 22   # blocks per launch of the row kernels before the launcher splits
+
+
+def test_row_kernels_past_grid_limit(moe):
+    """Permute, FP8 permute and combine over 2^22 + 3 tokens (one block per
+    token, so the launcher issues two launches with offset pointers): every
+    send row against its token's row, and sampled tokens on both sides of the
+    split against the oracle."""
+    T, H, k, E = MAX_ROW_BLOCKS + 3, 32, 2, 8
+    say(f"row kernels past the grid limit T={T} H={H} k={k}")
+    gen = torch.Generator(device=DEV).manual_seed(11)
+    x = torch.randint(-16000, 16000, (T, H), dtype=torch.int16, device=DEV, generator=gen)
+    x = (x & 0x3FFF).view(torch.bfloat16)                     # finite values below 2
+    res = torch.randn((T, H), device=DEV, generator=gen).to(torch.bfloat16)
+    # identity-like layout: replica j of token t goes to row j*T + t (distinct, dropless)
+    tt = torch.arange(T, dtype=torch.int32, device=DEV)
+    pos = torch.stack([tt, tt + T], dim=1).contiguous()
+    wt = torch.rand((T, k), device=DEV, generator=gen)
+    send = moe.moe_dispatch_permute(x, pos, E)
+    out = moe.moe_combine_reduce(send, pos, wt, None, res)
+    out32 = moe.moe_combine_reduce(send, pos, wt, None, res, out_fp32=True)
+    torch.cuda.synchronize()
+    xi = x.view(torch.int16)
+    assert torch.equal(send[:T].view(torch.int16), xi) and torch.equal(send[T:].view(torch.int16), xi)
+    sample = np.unique(np.concatenate([np.arange(4), np.arange(MAX_ROW_BLOCKS - 4, T),
+                                       np.random.default_rng(3).integers(0, T, 200)]))
+    s = torch.from_numpy(sample).to(DEV)
+    xs, rs = down_u16(x[s]), down_u16(res[s])
+    ws = wt[s].cpu().numpy().astype(np.float64)
+    npos = np.stack([np.arange(len(sample)), np.arange(len(sample)) + len(sample)], 1).astype(np.int32)
+    ref = oracle.combine_reduce(np.concatenate([xs, xs]), npos, ws, None, rs)
+    got32 = out32[s].cpu().numpy().astype(np.float64)
+    assert np.abs(got32 - ref).max() <= 1e-5
+    assert_bf16_close(down_u16(out[s]), oracle.bf16_round(ref), 1e-5, err_msg="combine past the grid limit")
+    send8 = moe.moe_dispatch_permute_fp8(x, pos, E)
+    torch.cuda.synchronize()
+    rows8 = oracle.dispatch_permute_fp8(xs, np.arange(len(sample), dtype=np.int32).reshape(-1, 1), len(sample))
+    np.testing.assert_array_equal(send8[s].cpu().numpy(), rows8)
+    np.testing.assert_array_equal(send8[s + T].cpu().numpy(), rows8)
+
+
+def test_route_past_grid_limit(moe):
+    """The routing kernel over 2^24 + 5 tokens of 256 experts (one wave per
+    token, four per block: past 2^22 blocks the launcher splits the tokens):
+    sampled tokens on both sides of the split against the oracle."""
+    T, E, k = 4 * MAX_ROW_BLOCKS + 5, 256, 2
+    say(f"route past the grid limit T={T} E={E} k={k}")
+    gen = torch.Generator(device=DEV).manual_seed(12)
+    logits = torch.randn((T, E), device=DEV, generator=gen)
+    idx, wt = moe.moe_route_topk(logits, None, k)
+    torch.cuda.synchronize()
+    cut = 4 * MAX_ROW_BLOCKS
+    sample = np.unique(np.concatenate([np.arange(3), np.arange(cut - 3, T),
+                                       np.random.default_rng(4).integers(0, T, 300)]))
+    s = torch.from_numpy(sample).to(DEV)
+    lg = logits[s].cpu().numpy()
+    o_idx, o_w = oracle.route_topk(lg, None, k)
+    np.testing.assert_array_equal(idx[s].cpu().numpy(), o_idx)
+    assert np.all(np.abs(wt[s].cpu().numpy() - o_w) <= weight_tolerance(lg, o_idx, o_w, k))
+    del logits
