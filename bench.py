@@ -801,10 +801,12 @@ def main(argv=None):
         summarize(args.summarize)
         return
     if args.write_traffic:
-        cmds = [f"cd /tmp && export TMPDIR=/tmp && rocprofv3 --pmc {c} -d $GRAFT_REPO_ROOT/gpurun_out/{d} -o run "
-                f"--output-format csv -- python3 $GRAFT_REPO_ROOT/bench.py --workload {args.workload} --steps 2 "
-                f"--warmup 1 --also '' --no-cpu-baseline --no-tile-return --no-floor --calibrate"
-                for c, d in (("FETCH_SIZE", "pmc_fetch"), ("WRITE_SIZE", "pmc_write"))]
+        # the counter runs as made from the repository root, into the two
+        # directories this call reads
+        cmds = [f"rocprofv3 --pmc {c} -d {d} -o run --output-format csv -- python3 bench.py --workload "
+                f"{args.workload} --steps 2 --warmup 1 --also '' --no-cpu-baseline --no-tile-return --no-floor "
+                f"--calibrate"
+                for c, d in (("FETCH_SIZE", args.write_traffic[0]), ("WRITE_SIZE", args.write_traffic[1]))]
         write_traffic(args.write_traffic[0], args.write_traffic[1], workload_by_name(args.workload).name, cmds)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:

@@ -671,3 +671,39 @@ def test_route_past_grid_limit(moe):
     np.testing.assert_array_equal(idx[s].cpu().numpy(), o_idx)
     assert np.all(np.abs(wt[s].cpu().numpy() - o_w) <= weight_tolerance(lg, o_idx, o_w, k))
     del logits
+
+
+@pytest.mark.parametrize("cfg", [3, 5])
+def test_split_batch_matches_whole(moe, cfg):
+    """Grid-size independence: routing, permute and combine of a workload in
+    one launch each, and of its two halves in separate launches (a grid of
+    half the blocks each, on offset views), give the same bits token by
+    token."""
+    w = synthetic.WORKLOADS[cfg]
+    d = inputs(cfg)
+    ref = oracle_path(cfg)
+    say("split batch", w.describe())
+    lg = up(d["logits"])
+    x, res = up(d["x"], True), up(d["residual"], True)
+    sh = None if d["shared"] is None else up(d["shared"], True)
+    idx, wt = moe.moe_route_topk(lg, None, w.k)
+    h = w.T // 2 + 1                                            # halves of unequal size
+    idx_a, wt_a = moe.moe_route_topk(lg[:h], None, w.k)
+    idx_b, wt_b = moe.moe_route_topk(lg[h:], None, w.k)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([idx_a, idx_b]), idx)
+    assert torch.equal(torch.cat([wt_a, wt_b]).view(torch.int32), wt.view(torch.int32))
+    pos = up(ref["L"]["pos"])
+    rows = send_rows_bound(w)
+    send = moe.moe_dispatch_permute(x, pos, w.E, w.capacity)
+    send2 = torch.full_like(send.view(torch.int16), 0x5A5A).view(torch.bfloat16)
+    # each half writes its own tokens' rows (both halves stay within the bound)
+    moe.moe_dispatch_permute(x[:h], pos[:h], w.E, w.capacity, send=send2, send_rows=rows)
+    moe.moe_dispatch_permute(x[h:], pos[h:], w.E, w.capacity, send=send2, send_rows=rows)
+    out = moe.moe_combine_reduce(send, pos, wt, sh, res)
+    out_a = moe.moe_combine_reduce(send, pos[:h], wt[:h], None if sh is None else sh[:h], res[:h])
+    out_b = moe.moe_combine_reduce(send, pos[h:], wt[h:], None if sh is None else sh[h:], res[h:])
+    torch.cuda.synchronize()
+    N = ref["N"]
+    assert torch.equal(send2[:N].view(torch.int16), send[:N].view(torch.int16))
+    assert torch.equal(torch.cat([out_a, out_b]).view(torch.int16), out.view(torch.int16))
