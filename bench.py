@@ -120,6 +120,8 @@ def parse(argv=None):
     p.add_argument("--no-cold", action="store_true",
                    help="skip the cold-cache pass (each step after a 1 GiB scratch read)")
     p.add_argument("--no-floor", action="store_true", help="skip the synthetic floor")
+    p.add_argument("--no-token-order", action="store_true",
+                   help="skip the permute and combine timed with every token's rows in token order")
     p.add_argument("--no-pipelined", action="store_true",
                    help="skip the pass with two batches in flight on two streams")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8-payload step (next_rows)")
@@ -258,29 +260,33 @@ def summarize(directory):
         raise SystemExit(f"no *kernel_stats.csv under {directory}")
     print("| kernel | calls | average us | min us | max us | total % |")
     print("|---|---|---|---|---|---|")
-    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+    # PyTorch's and the runtime's own kernels (input upload, bookkeeping) are left out
+    ours = [r for r in stats if not r["Name"].startswith(("at::", "void at::", "__amd_rocclr"))]
+    for r in sorted(ours, key=lambda r: -float(r["TotalDurationNs"])):
         print(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
               f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.2f} |")
-    # the floor kernel runs at several byte mixes under one name, one pass
-    # after another (the benchmark's order: step, permute, combine,
-    # write-only): split it into its passes, a pass being a run of launches
-    # with one grid that no other floor launch interrupts
+    # the floor kernel runs at several byte mixes, one pass after another
+    # (the benchmark's order: step, permute, combine, write-only), each with
+    # non-temporal then ordinary stores: split it into its passes, a pass
+    # being a run of launches of one instance with one grid
     trace = sorted(_csv_rows(directory, "kernel_trace.csv"), key=lambda r: int(r["Start_Timestamp"]))
     passes = []
     for r in trace:
-        if not _short(r["Kernel_Name"]).startswith("floor_kernel"):
+        name = _short(r["Kernel_Name"])
+        if not name.startswith("floor_kernel"):
             continue
-        grid = int(r["Grid_Size_X"])
-        if not passes or passes[-1][0] != grid:
-            passes.append((grid, []))
+        key = (int(r["Grid_Size_X"]), name)
+        if not passes or passes[-1][0] != key:
+            passes.append((key, []))
         passes[-1][1].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
     if passes:
         names = ["step", "permute", "combine", "write-only"]
-        print("\n| floor pass (benchmark order) | grid (threads) | calls | average us |")
-        print("|---|---|---|---|")
-        for i, (grid, v) in enumerate(passes):
-            label = names[i % 4] if len(passes) % 4 == 0 else str(i)
-            print(f"| {label} | {grid} | {len(v)} | {sum(v) / len(v):.2f} |")
+        print("\n| floor pass (benchmark order) | stores | grid (threads) | calls | average us |")
+        print("|---|---|---|---|---|")
+        for i, ((grid, name), v) in enumerate(passes):
+            label = names[(i // 2) % 4] if len(passes) % 8 == 0 else str(i)
+            kind = "non-temporal" if "<true>" in name else "ordinary"
+            print(f"| {label} | {kind} | {grid} | {len(v)} | {sum(v) / len(v):.2f} |")
 
 
 def _counter_means(directory, counter):
@@ -445,17 +451,24 @@ def per_call_ms(torch, stream, calls, steps):
             for i, (name, _) in enumerate(calls)}
 
 
-def floor_rate(moe, torch, stream, read_bytes, write_bytes, steps, warmup):
-    """moe_hbm_floor timed like the step: mean us per launch and GB/s."""
+def floor_rate(moe, torch, stream, read_bytes, write_bytes, steps, warmup, stores=("nt", "plain")):
+    """moe_hbm_floor timed like the step, once with each store kind in
+    `stores` (non-temporal, ordinary): the faster one's mean us per launch
+    and GB/s, and both times."""
     read_bytes, write_bytes = read_bytes // 16 * 16, write_bytes // 16 * 16
     src = torch.empty(max(read_bytes, 16), dtype=torch.uint8, device="cuda")
     dst = torch.empty(max(write_bytes, 16), dtype=torch.uint8, device="cuda")
-    ms = timed(torch, stream, lambda: moe.moe_hbm_floor(src, read_bytes, dst, write_bytes, stream=stream),
-               steps, warmup)
+    us = {}
+    for kind in stores:
+        ms = timed(torch, stream, lambda: moe.moe_hbm_floor(src, read_bytes, dst, write_bytes,
+                                                            nt_store=kind == "nt", stream=stream),
+                   steps, warmup)
+        us[kind] = round(ms * 1e3, 2)
     del src, dst
+    best = min(us, key=us.get)
     total = read_bytes + write_bytes
-    return {"read_bytes": read_bytes, "write_bytes": write_bytes, "us": round(ms * 1e3, 2),
-            "GBps": round(total / (ms * 1e-3) / 1e9, 1)}
+    return {"read_bytes": read_bytes, "write_bytes": write_bytes, "us": us[best],
+            "GBps": round(total / (us[best] * 1e-6) / 1e9, 1), "stores": best, "us_by_stores": us}
 
 
 def measure_path(moe, torch, w, args, groups=None, full=True):
@@ -541,8 +554,20 @@ def measure_path(moe, torch, w, args, groups=None, full=True):
         fl["value_frac_of_floor"] = round(gbps / fl["step"]["GBps"], 4)
         fl["permute_frac_of_floor"] = round(fl["permute"]["us"] / (pc["permute"] * 1e3), 4)
         fl["combine_frac_of_floor"] = round(fl["combine"]["us"] / (pc["combine"] * 1e3), 4)
-        fl["note"] = ("moe_hbm_floor: contiguous 16-byte streams of the same read and write bytes; "
-                      "write_only = the permute's write bytes alone; *_frac_of_floor = floor time / call time")
+        fl["note"] = ("moe_hbm_floor: contiguous 16-byte streams of the same read and write bytes, the faster "
+                      "of non-temporal and ordinary stores; write_only = the permute's write bytes alone; "
+                      "*_frac_of_floor = floor time / call time; token_order_rows_us = permute and combine "
+                      "with token t's replicas at rows t*k+j (dropless workloads only)")
+        if st.send_rows >= T * k and N == T * k and not args.no_token_order:
+            # the same row kernels and bytes with token t's replicas at rows
+            # t*k .. t*k + k - 1: every write in token order, no expert grouping
+            o = dict(st.main)
+            o["lay"] = dict(lay, pos=torch.arange(T * k, dtype=torch.int32, device=lay["pos"].device).view(T, k))
+            rows = [c for c in st.calls(stream.cuda_stream, o) if c[0] in ("permute", "combine")]
+            pcs = per_call_ms(torch, stream, rows, args.steps)
+            fl["token_order_rows_us"] = {n: round(v * 1e3, 2) for n, v in pcs.items()}
+            step()
+            torch.cuda.synchronize()
         res["synthetic_floor"] = fl
         log("synthetic floor", fl)
 
@@ -860,7 +885,8 @@ def main(argv=None):
     calibration = None
     if args.calibrate:
         # the floor kernel as a plain 1 GiB copy: the launch counter runs are scaled by
-        calibration = floor_rate(moe, torch, stream, FLOOR_CALIBRATION_BYTES, FLOOR_CALIBRATION_BYTES, 3, 1)
+        calibration = floor_rate(moe, torch, stream, FLOOR_CALIBRATION_BYTES, FLOOR_CALIBRATION_BYTES, 3, 1,
+                                 stores=("nt",))
         log("calibration copy", calibration)
 
     result = {
