@@ -5,6 +5,7 @@
 #pragma once
 
 #include "device.hpp"
+#include "launch.hpp"
 
 namespace moe {
 namespace {
@@ -12,6 +13,37 @@ namespace {
 // Assignments are read kBatch steps of 64 at a time, so that each wave has
 // kBatch independent loads in flight instead of one load per step.
 constexpr int kBatch = 8;
+
+// Rank one step of 64 consecutive assignments a0 + lane (the lane's id e;
+// lanes at or past a_end hold -1) in order. `run` is the wave's LDS row: its
+// next rank per expert, advanced past the step. Writes pos and send_src.
+__device__ __forceinline__ void rank_step(int32_t e, int64_t a0, int64_t a_end, int32_t k,
+                                          int32_t E, int32_t capacity, int nbits, int32_t *run,
+                                          const int32_t *eoff, int32_t *__restrict__ pos,
+                                          int32_t *__restrict__ send_src)
+{
+    const int64_t a = a0 + lane_id();
+    const bool valid = (uint32_t)e < (uint32_t)E;
+    uint64_t same = ballot64(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t ones = ballot64(bit);
+        same &= bit ? ones : ~ones;
+    }
+    const int32_t below = (int32_t)count_below(same);
+    const int32_t seen = valid ? run[e] : 0;
+    if (valid && below == 0)
+        run[e] = seen + (int32_t)__popcll(same);
+    if (a < a_end) {
+        const int32_t r = seen + below;
+        int32_t p = -1;
+        if (valid && (capacity < 0 || r < capacity))
+            p = eoff[e] + r;
+        pos[a] = p;
+        if (p >= 0 && send_src)
+            send_src[p] = (int32_t)((uint32_t)a / (uint32_t)k);
+    }
+}
 
 // Rank the assignments [a_begin, a_end) of one wave in order. `run` is the
 // wave's LDS row: on entry its first rank per expert, on exit advanced past
@@ -34,28 +66,8 @@ __device__ __forceinline__ void rank_range(const int32_t *__restrict__ idx, int6
         for (int s = 0; s < kBatch; ++s) {
             if (a0 + s * kWave >= a_end)
                 break;  // uniform: the wave's range is exhausted
-            const int64_t a = a0 + s * kWave + lane;
-            const int32_t e = ev[s];
-            const bool valid = (uint32_t)e < (uint32_t)E;
-            uint64_t same = ballot64(valid);
-            for (int b = 0; b < nbits; ++b) {
-                const bool bit = (e >> b) & 1;
-                const uint64_t ones = ballot64(bit);
-                same &= bit ? ones : ~ones;
-            }
-            const int32_t below = (int32_t)count_below(same);
-            const int32_t seen = valid ? run[e] : 0;
-            if (valid && below == 0)
-                run[e] = seen + (int32_t)__popcll(same);
-            if (a < a_end) {
-                const int32_t r = seen + below;
-                int32_t p = -1;
-                if (valid && (capacity < 0 || r < capacity))
-                    p = eoff[e] + r;
-                pos[a] = p;
-                if (p >= 0 && send_src)
-                    send_src[p] = (int32_t)((uint32_t)a / (uint32_t)k);
-            }
+            rank_step(ev[s], a0 + s * kWave, a_end, k, E, capacity, nbits, run, eoff, pos,
+                      send_src);
         }
     }
 }
@@ -151,10 +163,11 @@ __device__ __forceinline__ void wave_span(int64_t begin, int64_t end, int w, int
 }
 
 // The whole layout of TK <= kSmallAssignments assignments (E <= 512) in one
-// block of THREADS threads: each wave counts a contiguous range into its own
-// LDS row (pass A), a prefix over the waves and a block scan give the first
-// ranks and the offsets, then each wave ranks its range in order (pass B).
-// sm holds (THREADS / 64 + 2) * E + 1 ints.
+// block of THREADS threads. Each wave loads its contiguous range of ids once
+// (at most kBatch steps of 64) and keeps them in registers: it counts them
+// into its own LDS row (pass A), a prefix over the waves and a block scan
+// give the first ranks and the offsets, then it ranks the same ids in order
+// (pass B). sm holds (THREADS / 64 + 2) * E + 1 ints.
 template <int THREADS>
 __device__ __forceinline__ void layout_small_body(
     const int32_t *__restrict__ idx, int64_t TK, int32_t k, int32_t E, int32_t R,
@@ -165,19 +178,31 @@ __device__ __forceinline__ void layout_small_body(
 {
     constexpr int kSmallThreads = THREADS;
     constexpr int kSmallWaves = THREADS / kWave;
+    static_assert((int64_t)kSmallWaves * kBatch * kWave >= kSmallAssignments,
+                  "a wave's range must fit in its registers");
     int32_t *wh = sm;                           // [kSmallWaves][E]
     int32_t *cnt = wh + kSmallWaves * E;        // [E]
     int32_t *eoff = cnt + E;                    // [E + 1]
     __shared__ int32_t wave_total[kSmallWaves];
     const int tid = threadIdx.x;
     const int w = tid / kWave;
+    const int lane = lane_id();
 
+    int64_t lo, hi;
+    wave_span(0, TK, w, kSmallWaves, lo, hi);
+    int32_t ev[kBatch];
+#pragma unroll
+    for (int s = 0; s < kBatch; ++s) {
+        const int64_t a = lo + s * kWave + lane;
+        ev[s] = a < hi ? idx[a] : -1;
+    }
     for (int i = tid; i < kSmallWaves * E; i += kSmallThreads)
         wh[i] = 0;
     __syncthreads();
-    int64_t lo, hi;
-    wave_span(0, TK, w, kSmallWaves, lo, hi);
-    count_range(idx, lo, hi, lane_id(), kWave, E, wh + w * E);  // pass A
+#pragma unroll
+    for (int s = 0; s < kBatch; ++s)  // pass A
+        if ((uint32_t)ev[s] < (uint32_t)E)
+            atomicAdd(&wh[w * E + ev[s]], 1);
     __syncthreads();
     for (int e = tid; e < E; e += kSmallThreads) {
         int32_t run = 0;
@@ -195,7 +220,13 @@ __device__ __forceinline__ void layout_small_body(
     block_scan_counts<kSmallThreads>(cnt, E, eoff, wave_total);
     __syncthreads();
     publish_offsets(eoff, E, R, expert_offsets, dest_counts, dest_offsets);
-    rank_range(idx, lo, hi, k, E, capacity, nbits, wh + w * E, eoff, pos, send_src);  // pass B
+#pragma unroll
+    for (int s = 0; s < kBatch; ++s) {  // pass B
+        if (lo + s * kWave >= hi)
+            break;  // uniform: the wave's range is exhausted
+        rank_step(ev[s], lo + s * kWave, hi, k, E, capacity, nbits, wh + w * E, eoff, pos,
+                  send_src);
+    }
 }
 
 }  // namespace
