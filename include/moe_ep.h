@@ -200,11 +200,15 @@ moe_status_t moe_dispatch_layout(const int32_t *topk_idx, int64_t T,
  *   topk_w) and of moe_dispatch_layout (R, capacity and its outputs), plus
  *   workspace  device memory of at least
  *              moe_route_dispatch_layout_workspace_size() bytes (16 or
- *              more), 16-byte aligned. Its contents on entry do not matter:
- *              a call on a workspace its predecessor did not leave ready
- *              counts arrivals with a slower, stamp-keyed protocol, and
- *              every call leaves it ready. Calls that overlap in time must
- *              not share a workspace.
+ *              more), 16-byte aligned. Its contents on entry do not
+ *              matter, with one exception: a call on a workspace its
+ *              predecessor did not leave ready counts arrivals with a
+ *              slower, stamp-keyed protocol, and every call leaves it
+ *              ready; the exception is a first 64-bit word whose upper
+ *              half holds the ready pattern 0x6D6F6574 and whose lower
+ *              half is not 0 (no call leaves it so), which the call would
+ *              take as arrivals already counted. Calls that overlap in
+ *              time must not share a workspace.
  * Errors: those of the two calls; MOE_ERR_WORKSPACE when the workspace is
  *   NULL, misaligned or too small.
  */
