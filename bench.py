@@ -644,7 +644,7 @@ def measure_path(moe, torch, w, args, groups=None, full=True):
     return res, st, d, calls
 
 
-def bench_regroup(moe, torch, st, stream, warmup, steps):
+def bench_regroup(moe, torch, st, stream, warmup, steps, floor=True):
     """Receive-side regroup on this GPU's share: the send buffer read as a
     receive buffer of S = R source segments with E_l local experts each
     (counts = the layout's expert counts), regrouped expert-major and back.
@@ -691,11 +691,16 @@ def bench_regroup(moe, torch, st, stream, warmup, steps):
                         "frac": round(gbps["regroup"] / HBM_PEAK_GBPS, 4),
                         "traffic": stored_traffic("regroup_rows_kernel", w.name),
                         "algorithmic_bytes": nb["regroup"]}}
+    if floor:
+        # the synthetic floor for one direction's bytes (rows + recv_pos read, rows written)
+        fl = floor_rate(moe, torch, stream, N * H * 2 + N * 4, N * H * 2, steps, warmup)
+        out["synthetic_floor"] = fl
+        out["frac_of_floor"] = {n: round(fl["us"] / us[n], 4) for n in ("regroup", "ungroup")}
     log("regroup", out)
     return out
 
 
-def bench_fp8(moe, torch, st, calls, nbytes, stream, warmup, steps):
+def bench_fp8(moe, torch, st, calls, nbytes, stream, warmup, steps, floor=True):
     """The step with the FP8 dispatch payload: route -> layout ->
     moe_dispatch_permute_fp8 -> combine. The expert is the identity on the
     decoded rows: y = moe_fp8_dequant(send) is made once, before timing (a
@@ -744,6 +749,11 @@ def bench_fp8(moe, torch, st, calls, nbytes, stream, warmup, steps):
                            "algorithmic_bytes": nb["permute_fp8"]},
               "note": "send rows hold E4M3 codes plus one scale byte per 32 values; combine reads the "
                       "identity expert's bf16 output, decoded once before timing"}
+    if floor:
+        # the synthetic floor for the FP8 permute's own read and write bytes
+        fl = floor_rate(moe, torch, stream, T * k * 4 + T_read * H * 2, N * rb, steps, warmup)
+        report["synthetic_floor"] = fl
+        report["permute_fp8_frac_of_floor"] = round(fl["us"] / us["permute_fp8"], 4)
     log("fp8 dispatch", report)
     return report
 
@@ -854,9 +864,11 @@ def main(argv=None):
 
     next_rows = {}
     if not args.no_fp8 and w.H % 32 == 0:
-        next_rows["fp8_dispatch"] = bench_fp8(moe, torch, st, calls, nbytes, stream, args.warmup, args.steps)
+        next_rows["fp8_dispatch"] = bench_fp8(moe, torch, st, calls, nbytes, stream, args.warmup, args.steps,
+                                              floor=not args.no_floor)
     if not args.no_regroup and w.R >= 2:
-        next_rows["recv_regroup"] = bench_regroup(moe, torch, st, stream, args.warmup, args.steps)
+        next_rows["recv_regroup"] = bench_regroup(moe, torch, st, stream, args.warmup, args.steps,
+                                                  floor=not args.no_floor)
     if not args.no_tile_return and w.R >= 2 and w.H % 128 == 0:
         next_rows["tile_signalled_return"] = bench_tile_return(moe, torch, st, stream, args.warmup, args.steps)
     cpu_d = d
@@ -870,7 +882,8 @@ def main(argv=None):
         rx, stx, _, cx = measure_path(moe, torch, wx, args, groups, full=False)
         if wx.name in PREFILL and not args.no_fp8 and wx.H % 32 == 0:
             nbx = algorithmic_bytes(wx, rx["kept_rows"], rx["tokens_read"], stx.bias is not None)
-            rx["fp8_dispatch"] = bench_fp8(moe, torch, stx, cx, nbx, stream, args.warmup, args.steps)
+            rx["fp8_dispatch"] = bench_fp8(moe, torch, stx, cx, nbx, stream, args.warmup, args.steps,
+                                               floor=not args.no_floor)
         if wx.name in PREFILL and not args.no_tile_return and wx.R >= 2 and wx.H % 128 == 0:
             rx["tile_signalled_return"] = bench_tile_return(moe, torch, stx, stream, args.warmup, args.steps)
         workloads[wx.name] = rx
