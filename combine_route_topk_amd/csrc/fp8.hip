@@ -28,6 +28,9 @@
 // neighbouring lanes (one DPP swap for their maximum). Four scale bytes are
 // packed per 8 lanes with ds_bpermute, collected in LDS, and the slab's
 // 128-byte scale line leaves as eight 16-byte stores per kept replica.
+// For k >= 4 each block also loads (and discards) its slab of token
+// t + kPrefetchTokens, so that the block reading it later finds it in a
+// cache, as the bf16 permute does (its header gives the measurements).
 #include "device.hpp"
 #include "launch.hpp"
 
@@ -37,6 +40,8 @@ namespace {
 constexpr int kRowThreads = 256;
 constexpr int kSlabValues = kRowThreads * 16;   // 4096 values per block
 constexpr int kScaleLine = kSlabValues / 32;    // 128 scale bytes per slab
+constexpr int64_t kPrefetchTokens = 4096;       // a multiple of 8: the reader's XCD
+constexpr int32_t kPrefetchMinK = 4;
 
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
@@ -73,23 +78,40 @@ __device__ __forceinline__ u32x2 encode8(u32x4 v, float mul)
     return out;
 }
 
+// T tokens in this launch; x and pos extend n_ahead tokens further (rows a
+// prefetch may touch); pf_dist: the prefetch distance in tokens, 0 for none
 __global__ __launch_bounds__(kRowThreads) void permute_fp8_kernel(
-    const u32x4 *__restrict__ x, const int32_t *__restrict__ pos, int32_t C32, int32_t k,
-    uint8_t *__restrict__ send, int64_t send_rows, int64_t row_bytes)
+    const u32x4 *__restrict__ x, const int32_t *__restrict__ pos, int64_t T, int64_t n_ahead,
+    int64_t pf_dist, int32_t C32, int32_t k, uint8_t *__restrict__ send, int64_t send_rows,
+    int64_t row_bytes)
 {
     __shared__ u32x4 line[kScaleLine / 16];
     const int64_t t = blockIdx.x;
     const int32_t c = blockIdx.y * kRowThreads + threadIdx.x;
     const int32_t *pr = pos + t * k;
+    // lanes past the row act on zeros: their scale byte is 0, the padding
+    const bool active = c < C32;
+    // prefetch of token t + pf_dist's slab, if that token keeps a replica
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t tf = t + pf_dist;
+    const bool ahead = pf_dist > 0 && tf < T + n_ahead;  // uniform across the block
+    const int32_t pf = ahead && lane < k ? pos[tf * k + lane] : -1;
+    u32x4 warm0 = {0u, 0u, 0u, 0u}, warm1 = warm0;
+    if (ahead && ballot64(pf >= 0 && pf < send_rows) != 0 && active) {
+        warm0 = x[(tf * C32 + c) * 2];
+        warm1 = x[(tf * C32 + c) * 2 + 1];
+    }
     bool any = false;
     for (int j = 0; j < k; ++j) {
         const int32_t p = pr[j];
         any |= p >= 0 && p < send_rows;
     }
-    if (!any)  // the same for the whole block: no thread reaches the barrier
+    if (!any) {  // the same for the whole block: no thread reaches the barrier
+        // the prefetched values are not needed; this keeps their loads
+        asm volatile("" ::"v"(warm0[0]), "v"(warm0[1]), "v"(warm0[2]), "v"(warm0[3]),
+                     "v"(warm1[0]), "v"(warm1[1]), "v"(warm1[2]), "v"(warm1[3]));
         return;
-    // lanes past the row act on zeros: their scale byte is 0, the padding
-    const bool active = c < C32;
+    }
     u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = v0;
     if (active) {
         v0 = x[(t * C32 + c) * 2];
@@ -102,7 +124,6 @@ __global__ __launch_bounds__(kRowThreads) void permute_fp8_kernel(
     const u32x2 a = encode8(v0, mul), b = encode8(v1, mul);
     const u32x4 codes = {a[0], a[1], b[0], b[1]};
     // lane 8i packs the scale bytes of quantisation blocks 4i..4i+3
-    const int lane = threadIdx.x & (kWave - 1);
     const uint32_t sbyte = (uint32_t)(e + 127);
     const int src = (lane + 2) << 2;
     const uint32_t b1 = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)sbyte);
@@ -126,6 +147,8 @@ __global__ __launch_bounds__(kRowThreads) void permute_fp8_kernel(
                              threadIdx.x,
                          scales);
     }
+    asm volatile("" ::"v"(warm0[0]), "v"(warm0[1]), "v"(warm0[2]), "v"(warm0[3]), "v"(warm1[0]),
+                 "v"(warm1[1]), "v"(warm1[2]), "v"(warm1[3]));
 }
 
 // out[i] = bf16(value(code) * 2^(scale - 127)) for rows i < min(*n_rows, max_rows)
@@ -169,13 +192,14 @@ hipError_t launch_dispatch_permute_fp8(const uint16_t *x, const int32_t *pos, in
                                        hipStream_t stream)
 {
     const int32_t C32 = H / 16;
+    const int64_t pf_dist = k >= kPrefetchMinK ? kPrefetchTokens : 0;
     // one block per token; past kMaxRowBlocks tokens, one launch per chunk
     for (int64_t t0 = 0; t0 < T; t0 += kMaxRowBlocks) {
         const int64_t n = T - t0 < kMaxRowBlocks ? T - t0 : kMaxRowBlocks;
         const dim3 grid((unsigned)n, (unsigned)((H + kSlabValues - 1) / kSlabValues));
         hipLaunchKernelGGL(permute_fp8_kernel, grid, dim3(kRowThreads), 0, stream,
-                           reinterpret_cast<const u32x4 *>(x) + t0 * C32 * 2, pos + t0 * k, C32,
-                           k, send, send_rows, fp8_row_bytes(H));
+                           reinterpret_cast<const u32x4 *>(x) + t0 * C32 * 2, pos + t0 * k, n,
+                           T - t0 - n, pf_dist, C32, k, send, send_rows, fp8_row_bytes(H));
         const hipError_t err = hipGetLastError();
         if (err != hipSuccess)
             return err;
