@@ -608,18 +608,62 @@ def test_route_grouped_ties_and_specials(moe, E, k, G, M):
 
 
 # ---------------------------------------------------------------------------
+# the permutes' prefetch of x (k >= 4, the token 4096 ahead): batches just
+# past the prefetch distance, tokens with every replica dropped, and
+# capacity limits, checked row by row against the oracle
+# ---------------------------------------------------------------------------
+
+PREFETCH_TOKENS = 4096   # tokens ahead that a permute block loads for k >= 4
+
+
+@pytest.mark.parametrize("T,k,capacity", [
+    (PREFETCH_TOKENS + 1, 4, -1),       # one token past the distance
+    (PREFETCH_TOKENS + 13, 8, 40),      # capacity: most late tokens fully dropped
+    (3 * PREFETCH_TOKENS + 7, 5, 300),  # several distances, partial drops
+    (2 * PREFETCH_TOKENS, 3, -1),       # k = 3: no prefetch, same results
+])
+def test_permutes_around_prefetch(moe, T, k, capacity):
+    H, E, R = 288, 64, 8  # H = 288: part of one slab, for both payloads
+    say(f"permutes around the prefetch T={T} k={k} capacity={capacity} H={H} E={E}")
+    rng = np.random.default_rng(T + k)
+    logits = rng.standard_normal((T, E)).astype(np.float32)
+    logits[:, :4] += 3.0  # skew: the first experts overflow a capacity
+    x = synthetic.normal_bf16(T, 1, (T, H))
+    idx, _ = oracle.route_topk(logits, None, k)
+    L = oracle.dispatch_layout(idx, E, R, capacity)
+    rows = T * k if capacity < 0 else min(T * k, E * capacity)
+    ref = oracle.dispatch_permute(x, L["pos"], rows, fill=0x5A5A)
+    if capacity >= 0:
+        dropped_tokens = int(np.all(L["pos"] < 0, axis=1).sum())
+        assert dropped_tokens > 0, "the case must hold tokens with every replica dropped"
+    pos = up(L["pos"])
+    send = torch.full((rows, H), 0x5A5A, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    moe.moe_dispatch_permute(up(x, True), pos, E, capacity, send=send)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(down_u16(send), ref)
+    rb = oracle.fp8_row_bytes(H)
+    ref8 = oracle.dispatch_permute_fp8(x, L["pos"], rows, rb, fill=0xA5)
+    send8 = torch.full((rows, rb), 0xA5, dtype=torch.uint8, device=DEV)
+    moe.moe_dispatch_permute_fp8(up(x, True), pos, E, capacity, send=send8)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(send8.cpu().numpy(), ref8)
+
+
+# ---------------------------------------------------------------------------
 # token counts past the grid's limit: the launchers split the work
 # ---------------------------------------------------------------------------
 
 MAX_ROW_BLOCKS = 1 << 22   # blocks per launch of the row kernels before the launcher splits
 
 
-def test_row_kernels_past_grid_limit(moe):
+@pytest.mark.parametrize("k", [2, 4])
+def test_row_kernels_past_grid_limit(moe, k):
     """Permute, FP8 permute and combine over 2^22 + 3 tokens (one block per
     token, so the launcher issues two launches with offset pointers): every
     send row against its token's row, and sampled tokens on both sides of the
-    split against the oracle."""
-    T, H, k, E = MAX_ROW_BLOCKS + 3, 32, 2, 8
+    split against the oracle. With k = 4 the permutes' prefetch of the token
+    4096 ahead reaches across the split into the second launch's tokens."""
+    T, H, E = MAX_ROW_BLOCKS + 3, 32, 8
     say(f"row kernels past the grid limit T={T} H={H} k={k}")
     gen = torch.Generator(device=DEV).manual_seed(11)
     x = torch.randint(-16000, 16000, (T, H), dtype=torch.int16, device=DEV, generator=gen)
@@ -627,29 +671,33 @@ def test_row_kernels_past_grid_limit(moe):
     res = torch.randn((T, H), device=DEV, generator=gen).to(torch.bfloat16)
     # identity-like layout: replica j of token t goes to row j*T + t (distinct, dropless)
     tt = torch.arange(T, dtype=torch.int32, device=DEV)
-    pos = torch.stack([tt, tt + T], dim=1).contiguous()
+    pos = torch.stack([tt + j * T for j in range(k)], dim=1).contiguous()
     wt = torch.rand((T, k), device=DEV, generator=gen)
     send = moe.moe_dispatch_permute(x, pos, E)
     out = moe.moe_combine_reduce(send, pos, wt, None, res)
     out32 = moe.moe_combine_reduce(send, pos, wt, None, res, out_fp32=True)
     torch.cuda.synchronize()
     xi = x.view(torch.int16)
-    assert torch.equal(send[:T].view(torch.int16), xi) and torch.equal(send[T:].view(torch.int16), xi)
+    for j in range(k):
+        assert torch.equal(send[j * T:(j + 1) * T].view(torch.int16), xi), f"replica {j}"
+    del send
     sample = np.unique(np.concatenate([np.arange(4), np.arange(MAX_ROW_BLOCKS - 4, T),
                                        np.random.default_rng(3).integers(0, T, 200)]))
     s = torch.from_numpy(sample).to(DEV)
     xs, rs = down_u16(x[s]), down_u16(res[s])
     ws = wt[s].cpu().numpy().astype(np.float64)
-    npos = np.stack([np.arange(len(sample)), np.arange(len(sample)) + len(sample)], 1).astype(np.int32)
-    ref = oracle.combine_reduce(np.concatenate([xs, xs]), npos, ws, None, rs)
+    n = len(sample)
+    npos = np.stack([np.arange(n) + j * n for j in range(k)], 1).astype(np.int32)
+    ref = oracle.combine_reduce(np.concatenate([xs] * k), npos, ws, None, rs)
     got32 = out32[s].cpu().numpy().astype(np.float64)
     assert np.abs(got32 - ref).max() <= 1e-5
     assert_bf16_close(down_u16(out[s]), oracle.bf16_round(ref), 1e-5, err_msg="combine past the grid limit")
+    del out, out32
     send8 = moe.moe_dispatch_permute_fp8(x, pos, E)
     torch.cuda.synchronize()
-    rows8 = oracle.dispatch_permute_fp8(xs, np.arange(len(sample), dtype=np.int32).reshape(-1, 1), len(sample))
-    np.testing.assert_array_equal(send8[s].cpu().numpy(), rows8)
-    np.testing.assert_array_equal(send8[s + T].cpu().numpy(), rows8)
+    rows8 = oracle.dispatch_permute_fp8(xs, np.arange(n, dtype=np.int32).reshape(-1, 1), n)
+    for j in range(k):
+        np.testing.assert_array_equal(send8[s + j * T].cpu().numpy(), rows8)
 
 
 def test_route_past_grid_limit(moe):
