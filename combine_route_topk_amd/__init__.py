@@ -18,7 +18,9 @@ from typing import Optional
 import torch
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libmoe_ep.so")
+# MOE_EP_LIB points the binding at another build of the same sources (the
+# host-sanitizer test loads one whose host code is built with AddressSanitizer)
+LIB_PATH = os.environ.get("MOE_EP_LIB") or os.path.join(_PKG, "libmoe_ep.so")
 
 MOE_OK = 0
 MOE_ERR_INVALID_ARG = 1

@@ -534,6 +534,8 @@ const char *moe_status_string(moe_status_t status)
         return "MOE_ERR_WORKSPACE: workspace missing or too small";
     case MOE_ERR_LAUNCH:
         return "MOE_ERR_LAUNCH: kernel launch failed";
+    default:
+        break;
     }
     return "unknown moe_status_t";
 }

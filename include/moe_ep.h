@@ -44,7 +44,12 @@ typedef enum moe_status {
     MOE_ERR_INVALID_ARG = 1,  /* NULL/misaligned pointer, bad size or relation */
     MOE_ERR_UNSUPPORTED = 2,  /* outside the limits above */
     MOE_ERR_WORKSPACE = 3,    /* workspace missing or too small */
-    MOE_ERR_LAUNCH = 4        /* the HIP runtime rejected a kernel launch */
+    MOE_ERR_LAUNCH = 4,       /* the HIP runtime rejected a kernel launch */
+    /* not a status: gives the type the range of a 32-bit int, so that any
+       int value passed as a moe_status_t (moe_status_string of an unknown
+       code) is a valid value of the type in C++ as well as in C */
+    MOE_STATUS_RANGE_MIN = -0x7FFFFFFF - 1,
+    MOE_STATUS_RANGE_MAX = 0x7FFFFFFF
 } moe_status_t;
 
 /* moe_route_topk flags */
