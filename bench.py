@@ -35,8 +35,12 @@ The synthetic floor is moe_hbm_floor: a hand-written contiguous streaming
 kernel that reads and writes given byte counts with the row kernels' 16-byte
 lane accesses and nothing else. It is timed like the step at the step's own
 read and write volumes, and at each of the permute's and the combine's, plus
-a write-only stream of the permute's write bytes (the write ceiling). The
-gap between a call and its floor is overhead the path owns.
+a write-only stream of the permute's write bytes (the write ceiling), each
+with non-temporal and with ordinary stores, keeping the faster. The gap
+between a call and its floor is overhead the path owns. On dropless
+workloads the permute and the combine are also timed with every token's
+replicas at rows t*k .. t*k + k - 1 ("token_order_rows_us"), which
+separates the cost of the layout's scattered rows from the kernels' own.
 
 After the path, further measurements are reported under "next_rows", none
 part of `value`:
