@@ -207,3 +207,30 @@ def test_graph_replay(moe, cfg):
                 b = b.view(torch.int16 if b.element_size() == 2 else torch.int32)
             assert torch.equal(a, b), f"replay {rep}: {n} differs from the eager step"
         assert int(ws[:8].view(torch.int64).item()) == READY
+
+
+@pytest.mark.parametrize("T,E,k,R", [(128, 256, 8, 32), (512, 64, 8, 8), (4096, 128, 1, 16)])
+def test_back_to_back_calls_see_new_ids(moe, T, E, k, R):
+    """64 calls in a row on one stream and one workspace, each on new logits
+    written just before it: the last block of each call must build the
+    layout from that call's ids, which the other blocks release through the
+    ticket's read-modify-write. Every call is compared with the two
+    separate calls on the same logits; a layout built from ids of the call
+    before would differ."""
+    say(f"back-to-back fused calls T={T} E={E} k={k} R={R}")
+    gen = torch.Generator(device=DEV).manual_seed(T + E)
+    ws = torch.empty(moe.moe_route_dispatch_layout_workspace_size(T, E, k, R), dtype=torch.uint8, device=DEV)
+    outs, refs = [], []
+    for i in range(64):
+        lg = torch.randn((T, E), device=DEV, generator=gen)
+        F = moe.moe_route_dispatch_layout(lg, None, k, R, -1, workspace=ws)
+        idx, wt = moe.moe_route_topk(lg, None, k)
+        L = moe.moe_dispatch_layout(idx, E, R, -1)
+        outs.append(F)
+        refs.append((idx, wt, L))
+    torch.cuda.synchronize()
+    for i, (F, (idx, wt, L)) in enumerate(zip(outs, refs)):
+        assert torch.equal(F["topk_idx"], idx), f"call {i}: ids"
+        assert torch.equal(F["topk_w"].view(torch.int32), wt.view(torch.int32)), f"call {i}: weights"
+        for n in LAYOUT + ("send_src",):
+            assert torch.equal(F[n], L[n]), f"call {i}: {n}"
